@@ -1,0 +1,20 @@
+"""The oracle against its pins (CPU only)."""
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return oracle.load()
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_oracle_pin(pin, lib):
+    pin(lib)
+
+
+def test_oracle_threads(lib):
+    assert oracle.num_threads(lib) >= 1

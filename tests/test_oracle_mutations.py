@@ -1,0 +1,58 @@
+"""The pins are sensitive: each plausible mistake planted in a copy of the
+oracle's C source (on the CPU, in a temporary directory) fails at least one pin.
+"""
+
+import os
+import shutil
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, original text, planted text); each original occurs exactly once.
+MUTATIONS = [
+    ("dropped scale", "s[j] = scale * acc;", "s[j] = acc;"),
+    ("dropped first term of the sum",
+     "for (int64_t j = 0; j < visible; ++j)\n                l += exp(s[j] - m);",
+     "for (int64_t j = 1; j < visible; ++j)\n                l += exp(s[j] - m);"),
+    ("wrong sign in the weight", "double p = exp(s[j] - m) / l;", "double p = exp(m - s[j]) / l;"),
+    ("causal off by one", "if (causal && i + 1 < M) visible = i + 1;", "if (causal && i + 2 < M) visible = i + 2;"),
+    ("K used in place of V", "oi[c] += p * vh[j * d + c];", "oi[c] += p * kh[j * d + c];"),
+    ("reversed feature index", "acc += qi[c] * kh[j * d + c];", "acc += qi[c] * kh[j * d + (d - 1 - c)];"),
+    ("LSE without the max", "lse_rows[t] = m + log(l);", "lse_rows[t] = log(l);"),
+    ("softmax without the divide", "yr[j] = exp(xr[j] - m) / s;", "yr[j] = exp(xr[j] - m);"),
+    ("softmax shifts by the min",
+     "double *yr = y + r * n;\n        /* pass 1: the maximum */\n        double m = xr[0];\n"
+     "        for (int64_t j = 1; j < n; ++j)\n            if (xr[j] > m) m = xr[j];",
+     "double *yr = y + r * n;\n        /* pass 1: the maximum */\n        double m = xr[0];\n"
+     "        for (int64_t j = 1; j < n; ++j)\n            if (xr[j] < m) m = xr[j];"),
+    ("normaliser without the rescale", "s = s * exp(m - m_new) + exp(xr[i] - m_new);", "s = s + exp(xr[i] - m_new);"),
+    ("normaliser rescale inverted", "s = s * exp(m - m_new) + exp(xr[i] - m_new);",
+     "s = s * exp(m_new - m) + exp(xr[i] - m_new);"),
+    ("normaliser starts at 0", "double s = 1.0;", "double s = 0.0;"),
+    ("LSE of softmax rows without the max", "lse[r] = m + log(s);", "lse[r] = log(s);"),
+    ("query row ignores the head", "const double *qi = q + r * d;", "const double *qi = q + i * d;"),
+    ("every head uses head 0's keys", "const double *kh = k + bh * M * d;", "const double *kh = k;"),
+]
+
+
+@pytest.mark.parametrize("name,orig,planted", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, orig, planted, tmp_path):
+    with open(SRC, encoding="utf-8") as f:
+        src = f.read()
+    assert src.count(orig) == 1, f"mutation anchor for {name!r} must occur exactly once"
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(orig, planted), encoding="utf-8")
+    so = oracle.build(out=str(tmp_path / "liboracle_mutant.so"), src=str(mutant), extra_flags=("-w",))
+    lib = oracle.load(so)
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError as e:
+            failures.append((pin.__name__, str(e).splitlines()[0]))
+    assert failures, f"planted mistake {name!r} passed every pin"
+    shutil.rmtree(tmp_path, ignore_errors=True)
