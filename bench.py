@@ -1,0 +1,226 @@
+"""Benchmark of the fused online-softmax attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+A step is one attn_fwd call over the whole workload (default: B=2, H=16,
+N=M=4096, d=128, bf16, causal -- the configuration the throughput target is
+stated on) with inputs already resident in HBM.  Prints ONE JSON line on
+stdout; progress goes to stderr.
+
+  value      attention-forward TFLOP/s, 4*N*M*d per head (halved for causal)
+             over the timed region
+  roofline   the attention kernel against the bf16 dense MFMA peak
+             (256 CUs x 2.4 GHz x 4096 flop/clk/CU = 2516.6 TFLOP/s); achieved
+             = algorithmic flops per launch / mean launch duration measured with
+             HIP events on the launch stream; traffic = HBM bytes per launch
+             from the committed rocprofv3 counter summary when it was taken on
+             the current kernel source, else null
+  cpu_baseline  the float64 oracle timed on this host's cores on a bounded,
+             evenly spaced sample of the same workload's query rows
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import seeded_inputs as si  # noqa: E402
+
+PEAKS_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["attn_bf16.hip", "attn_f32.hip", "attn_decode.hip", "attn_api.cpp", "kernels.h"]
+
+
+def err(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "online_softmax_10_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(w: si.Workload) -> float:
+    esz = 2 if w.dtype == "bf16" else 4
+    return w.B * w.H * ((w.N + 2 * w.M) * w.d * esz + w.N * w.d * esz + w.N * 4)
+
+
+def cpu_baseline(w: si.Workload, q, k, v, o_gpu, lse_gpu, target_s: float):
+    """Time the oracle on an evenly spaced sample of query rows (~target_s seconds)."""
+    import oracle
+
+    err(f"[bench] cpu baseline: oracle on {oracle.num_threads()} threads")
+    qf, kf, vf = (si.to_f64(a, w.dtype) for a in (q, k, v))
+    total = w.B * w.H * w.N
+
+    def row_flops(rows):
+        i = rows % w.N
+        vis = np.minimum(i + 1, w.M) if w.causal else np.full_like(i, w.M)
+        return float(np.sum(4.0 * w.d * vis))
+
+    def run(rows):
+        t0 = time.perf_counter()
+        o, lse = oracle.attention_rows(qf, kf, vf, w.scale, w.causal, rows)
+        return time.perf_counter() - t0, o, lse
+
+    probe = np.linspace(0, total - 1, 256).astype(np.int64)
+    dt, _, _ = run(probe)
+    rate = row_flops(probe) / max(dt, 1e-6)
+    count = int(min(total, max(256, 256 * target_s * rate / max(row_flops(probe), 1.0))))
+    rows = np.linspace(0, total - 1, count).astype(np.int64)
+    dt, o_ref, lse_ref = run(rows)
+    flops = row_flops(rows)
+    o_s = o_gpu.reshape(-1, w.d)[rows]
+    l_s = lse_gpu.reshape(-1)[rows]
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{count} of {total} query rows, evenly spaced over all heads and positions "
+                  f"({flops / 1e9:.2f} GFLOP, {dt:.1f} s)",
+        "seconds": dt,
+        "max_abs_err_vs_gpu": {"o": float(np.max(np.abs(o_s - o_ref))),
+                               "lse": float(np.max(np.abs(l_s - lse_ref)))},
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=sorted(si.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import online_softmax_10_amd as osa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = si.WORKLOADS[args.workload]
+    err(f"[bench] workload {w}")
+    q, k, v = si.make_qkv(w, args.seed)
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=tdtype, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+
+    def step():
+        osa.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = t_begin.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    err(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us), "
+        f"{value:.1f} TFLOP/s")
+
+    achieved = w.flops / (launch_ms * 1e-3) / 1e12
+    peak = PEAKS_TFLOPS[w.dtype]
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": load_traffic(w.name),
+        "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
+        "launch_us": round(launch_ms * 1e3, 2),
+        "algorithmic_bytes": algorithmic_bytes(w),
+        "hbm_gbs_algorithmic": round(algorithmic_bytes(w) / (launch_ms * 1e-3) / 1e9, 1),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        o_host = o.float().cpu().numpy().astype(np.float64)
+        l_host = lse.cpu().numpy().astype(np.float64)
+        cpu = cpu_baseline(w, q, k, v, o_host, l_host, args.cpu_seconds)
+
+    line = {
+        "metric": "attn fwd TFLOP/s at 1 GPU + % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} M={w.M} d={w.d} {w.dtype} "
+                               f"{'causal' if w.causal else 'non-causal'}, seed {args.seed}",
+                   "B": w.B, "H": w.H, "N": w.N, "M": w.M, "d": w.d, "causal": w.causal},
+        "pct_of_bf16_peak": round(100.0 * value / PEAKS_TFLOPS["bf16"], 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,147 @@
+/*
+ * attn.h -- C ABI of libattn.so, the MI355X (gfx950) online-softmax attention
+ * forward and row-wise online softmax.
+ *
+ * Plain C: pointers, sizes and a stream handle; no C++ or framework types.
+ * Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ * never frees, retains or reallocates it.  All calls are asynchronous on the
+ * given HIP stream (a hipStream_t passed as void*, NULL = the null stream) and
+ * never synchronise the host.  A return of ATTN_OK means "validated and
+ * enqueued": a fault while the kernels run surfaces at the caller's next
+ * synchronisation, as for any HIP launch.  Argument validation happens before
+ * any HIP call, so invalid arguments are reported without touching a device.
+ * No exception crosses this boundary.  The library keeps no global state
+ * besides a per-thread error detail string, so it is safe to call from
+ * several host threads.
+ */
+#ifndef ONLINE_SOFTMAX_ATTN_H
+#define ONLINE_SOFTMAX_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. */
+typedef enum {
+    ATTN_F32 = 0,  /* IEEE binary32 */
+    ATTN_BF16 = 1  /* bfloat16 (8-bit significand), stored as 16-bit words */
+} attn_dtype;
+
+/* Return codes. */
+enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,      /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = -2,     /* a size is negative, or M < 1 / n < 1 with work to do */
+    ATTN_ERR_HEADDIM = -3,   /* d is not one of the compiled head dims (64, 128) */
+    ATTN_ERR_DTYPE = -4,     /* dtype is not an attn_dtype */
+    ATTN_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
+    ATTN_ERR_OVERFLOW = -6,  /* sizes exceed the kernels' index range */
+    ATTN_ERR_HIP = -7,       /* a HIP launch or allocation failed (see attn_last_error_detail) */
+    ATTN_ERR_SCALE = -8,     /* scale is NaN or infinite */
+    ATTN_ERR_SPLITS = -9     /* num_splits outside [0, ATTN_MAX_SPLITS] */
+};
+
+/* Largest split count attn_fwd_splits accepts. */
+#define ATTN_MAX_SPLITS 256
+
+/*
+ * attn_fwd -- exact attention forward with the online-softmax recurrence.
+ *
+ * For every batch b < B, head h < H and query row i < N:
+ *   s_j   = scale * <q[b,h,i,:], k[b,h,j,:]>        for visible keys j,
+ *   o[b,h,i,:] = sum_j softmax(s)_j * v[b,h,j,:],
+ *   lse[b,h,i] = log sum_j e^{s_j}                  (natural log),
+ * computed block by block with a running max m and running exponential sum l
+ * that rescale the unnormalised accumulator by e^{m_old - m_new} whenever a
+ * new key block raises the max; the N x M score matrix never reaches memory.
+ * Source: "Online Softmax and Flash Attention" page, eq. (8) (definition and
+ * shapes Q [N,K], K and V [M,K]); "从原始Softmax到在线Softmax" page, the
+ * online softmax derivation (m, l, o~ recurrences, o = o~/l) and the LSE
+ * definition.
+ *
+ * Visible keys: all j < M when causal == 0; j <= i (and j < M) when causal != 0,
+ * i.e. key index greater than query index is masked, counted from 0 in both
+ * (top-left aligned when N != M).
+ *
+ * Arguments
+ *   q      [B,H,N,d] dtype, contiguous row-major        (device, read)
+ *   k, v   [B,H,M,d] dtype, contiguous row-major        (device, read)
+ *   o      [B,H,N,d] dtype, contiguous row-major        (device, written)
+ *   lse    [B,H,N] float32                              (device, written)
+ *   B, H, N >= 0 (B*H*N == 0 is a no-op returning ATTN_OK); M >= 1
+ *   d      head dim, 64 or 128 (compile-time instantiations)
+ *   scale  finite float32 used exactly as passed (1/sqrt(d) for the usual form)
+ *   causal 0 or non-zero
+ *   dtype  ATTN_F32 (fp32 products and accumulation throughout) or ATTN_BF16
+ *          (bf16 products, fp32 accumulation, probabilities rounded to bf16
+ *          before the P.V product, o rounded to nearest-even bf16)
+ *   stream hipStream_t as void*
+ * o must not overlap q, k, v or lse.  q, k, v, o and lse must be 16-byte
+ * aligned.  Per-head sizes N*d and M*d must each be below 2^31 elements and
+ * B*H below 2^31.
+ *
+ * Errors: ATTN_ERR_NULL, _SHAPE, _HEADDIM, _DTYPE, _ALIGN, _OVERFLOW, _SCALE
+ * before any HIP call; ATTN_ERR_HIP if a launch or the split workspace
+ * allocation fails.  Outputs are unspecified after an error.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             int64_t B, int64_t H, int64_t N, int64_t M, int d,
+             float scale, int causal, int dtype, void *stream);
+
+/*
+ * attn_fwd_splits -- attn_fwd with an explicit split count over the keys.
+ *
+ * num_splits == 0 lets the library choose (what attn_fwd does).  num_splits
+ * == 1 forces the single-pass kernel.  num_splits >= 2 divides the keys into
+ * that many contiguous ranges, computes each range's normalised partial
+ * output O_s and log-sum-exp lse_s, and merges them:
+ *   lse = log sum_s e^{lse_s},   o = sum_s e^{lse_s - lse} O_s,
+ * which is the block merge of the online recurrence (the "从原始Softmax到在线
+ * Softmax" page, merge form of the m / l / o~ update).  An empty range has
+ * lse_s = -inf and weight 0.  The partials live in a workspace allocated
+ * with hipMallocAsync and freed with hipFreeAsync on the same stream.
+ * Every split count gives the same result up to rounding.
+ *
+ * Arguments and errors as attn_fwd, plus ATTN_ERR_SPLITS when num_splits < 0
+ * or num_splits > ATTN_MAX_SPLITS.
+ */
+int attn_fwd_splits(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int64_t B, int64_t H, int64_t N, int64_t M, int d,
+                    float scale, int causal, int dtype, int num_splits, void *stream);
+
+/*
+ * online_softmax -- row-wise softmax with the one-pass normaliser.
+ *
+ * For each row r < rows of x [rows, n] (float32, row-major):
+ *   pass 1: running max m and running sum s over the row,
+ *           m_i = max(m_{i-1}, x_i), s_i = s_{i-1} e^{m_{i-1}-m_i} + e^{x_i-m_i},
+ *           kept per lane over strided elements and merged across lanes with
+ *           the same rule;
+ *   pass 2: y[r,i] = e^{x[r,i] - m} / s.
+ * Source: "Online Softmax and Flash Attention" page, section "Online softmax",
+ * eq. (3)-(7); "Softmax与Flash-Attention" page, online-softmax derivation.
+ *
+ * Arguments
+ *   x     [rows, n] float32 (device, read);  y [rows, n] float32 (device, written)
+ *   rows >= 0 (0 is a no-op), n >= 1 when rows > 0
+ *   stream hipStream_t as void*
+ * x and y must be 16-byte aligned and may be the same buffer (in place).
+ * rows * n must be below 2^62 and n below 2^31.
+ * Errors: ATTN_ERR_NULL, _SHAPE, _ALIGN, _OVERFLOW before any HIP call;
+ * ATTN_ERR_HIP if the launch fails.  A row whose entries are all -inf gives NaN.
+ */
+int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stream);
+
+/* Static, human-readable text for a return code (never NULL). */
+const char *attn_strerror(int code);
+
+/* Detail of the last ATTN_ERR_HIP on the calling thread ("" if none). */
+const char *attn_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONLINE_SOFTMAX_ATTN_H */

@@ -1,0 +1,137 @@
+"""Python binding of libattn.so: the MI355X online-softmax attention forward.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attn.h``; torch provides device
+memory and the stream.  There is no CPU or torch fallback: if the library is
+missing or a call fails, an exception is raised.
+
+    o, lse = fwd(q, k, v, scale=None, causal=False)      # q [B,H,N,d], k/v [B,H,M,d]
+    y = online_softmax(x)                                  # x [rows, n] float32
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["fwd", "fwd_splits", "online_softmax", "lib", "LIB_PATH", "AttnError",
+           "ATTN_F32", "ATTN_BF16", "ATTN_MAX_SPLITS", "EXPORTED_SYMBOLS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+ATTN_MAX_SPLITS = 256
+ERROR_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
+               -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_OVERFLOW", -7: "ATTN_ERR_HIP",
+               -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_SPLITS"}
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "online_softmax", "attn_strerror", "attn_last_error_detail")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        detail = ""
+        if _lib is not None:
+            detail = _lib.attn_strerror(code).decode()
+            if code == -7:
+                detail += f" [{_lib.attn_last_error_detail().decode()}]"
+        super().__init__(f"{where}: {ERROR_NAMES.get(code, code)}: {detail}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m online_softmax_10_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                               ctypes.c_int, ctypes.c_int, vp]
+        L.attn_fwd.restype = ctypes.c_int
+        L.attn_fwd_splits.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+        L.attn_fwd_splits.restype = ctypes.c_int
+        L.online_softmax.argtypes = [vp, vp, i64, i64, vp]
+        L.online_softmax.restype = ctypes.c_int
+        L.attn_strerror.argtypes = [ctypes.c_int]
+        L.attn_strerror.restype = ctypes.c_char_p
+        L.attn_last_error_detail.argtypes = []
+        L.attn_last_error_detail.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _stream_handle(device):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
+
+
+def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None):
+    """Attention forward with an explicit split count (0 = library's choice).
+
+    q [B,H,N,d], k and v [B,H,M,d]: contiguous CUDA/HIP tensors of one dtype
+    (bfloat16 or float32).  Returns (o [B,H,N,d] same dtype, lse [B,H,N] float32).
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B,H,rows,d]")
+    B, H, N, d = q.shape
+    M = k.shape[2]
+    if tuple(k.shape) != (B, H, M, d) or tuple(v.shape) != (B, H, M, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = lib().attn_fwd_splits(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, N, M, d, float(scale), int(bool(causal)), code, int(num_splits),
+                               _stream_handle(q.device))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_splits")
+    return out, lse
+
+
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """softmax(mask(q k^T * scale)) v and the row log-sum-exp (natural log)."""
+    return fwd_splits(q, k, v, scale=scale, causal=causal, num_splits=0, out=out, lse=lse)
+
+
+def online_softmax(x, out=None):
+    """Row-wise softmax of a contiguous float32 GPU tensor over its last axis."""
+    import torch
+
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    n = x.shape[-1] if x.dim() > 0 else 1
+    rows = x.numel() // n if n > 0 else 0
+    if out is None:
+        out = torch.empty_like(x)
+    rc = lib().online_softmax(x.data_ptr(), out.data_ptr(), rows, n, _stream_handle(x.device))
+    if rc != 0:
+        raise AttnError(rc, "online_softmax")
+    return out

@@ -1,0 +1,204 @@
+// C-ABI front end of libattn.so: argument validation (before any HIP call),
+// kernel selection, the split-count heuristic and the stream-ordered split
+// workspace.  The declarations and their contracts are in include/attn.h.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "attn.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxBlocks = int64_t(1) << 24;  // grid.x * 256 threads stays below 2^32
+constexpr int64_t kI32Max = 0x7fffffff;
+
+thread_local char g_detail[256] = "";
+
+void set_detail(const char *what, hipError_t e) {
+    snprintf(g_detail, sizeof(g_detail), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+struct Plan {
+    enum Kind { SINGLE, SPLIT, DECODE } kind;
+    int splits;
+    int tiles_per_split;  // in units of the chosen kernel's key tile
+};
+
+// Work decomposition.  num_splits: 0 = choose, 1 = single pass, >= 2 = split.
+Plan plan_for(int64_t BH, int64_t N, int64_t M, bool bf16, int num_splits) {
+    const bool few_queries = N <= osa::kDecodeMaxQueries;
+    if (num_splits == 1) return Plan{Plan::SINGLE, 1, 0};
+    if (few_queries) {
+        // Decode shape: stream K/V with enough workgroups in flight; each split
+        // keeps at least 256 keys.
+        const int tile = osa::kDecodeKeyTile;
+        int s = num_splits;
+        if (s == 0) {
+            s = ceil_div(2048, BH);
+            const int cap = ceil_div(M, 256);
+            if (s > cap) s = cap;
+            if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;
+            if (s < 1) s = 1;
+        }
+        const int tps = ceil_div(ceil_div(M, s), tile);
+        return Plan{Plan::DECODE, s, tps};
+    }
+    const int tile = bf16 ? osa::kBf16KeyTile : osa::kF32KeyTile;
+    const int row_tiles = ceil_div(N, 128);
+    int s = num_splits;
+    if (s == 0) {
+        // Split only when the query tiles alone cannot fill the 256 compute
+        // units and the key range is long enough to share out.
+        const int64_t wgs = BH * row_tiles;
+        if (wgs >= 256) return Plan{Plan::SINGLE, 1, 0};
+        s = ceil_div(512, wgs);
+        const int cap = ceil_div(M, 4 * tile);
+        if (s > cap) s = cap;
+        if (s > ATTN_MAX_SPLITS) s = ATTN_MAX_SPLITS;
+        if (s <= 1) return Plan{Plan::SINGLE, 1, 0};
+    }
+    const int tps = ceil_div(ceil_div(M, s), tile);
+    return Plan{Plan::SPLIT, s, tps};
+}
+
+int validate_attn(const void *q, const void *k, const void *v, const void *o, const float *lse, int64_t B,
+                  int64_t H, int64_t N, int64_t M, int d, float scale, int dtype, int num_splits) {
+    if (B < 0 || H < 0 || N < 0 || M < 0) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
+    if (B == 0 || H == 0 || N == 0) return ATTN_OK;  // nothing to compute
+    if (M < 1) return ATTN_ERR_SHAPE;
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+    if (B > kI32Max || H > kI32Max || B * H > kI32Max) return ATTN_ERR_OVERFLOW;
+    if (N > kI32Max / d || M > kI32Max / d) return ATTN_ERR_OVERFLOW;
+    if (B * H * ceil_div(N, 128) > kMaxBlocks) return ATTN_ERR_OVERFLOW;
+    return ATTN_OK;
+}
+
+int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H, int64_t N,
+             int64_t M, int d, float scale, int causal, int dtype, int num_splits, void *stream_v) {
+    const int rc = validate_attn(q, k, v, o, lse, B, H, N, M, d, scale, dtype, num_splits);
+    if (rc != ATTN_OK || B == 0 || H == 0 || N == 0) return rc;
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    const bool bf16 = dtype == ATTN_BF16;
+    const int64_t BH = B * H;
+
+    osa::AttnProblem p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.BH = (int)BH;
+    p.N = (int)N;
+    p.M = (int)M;
+    p.d = d;
+    p.c = fabsf(scale) * 1.4426950408889634f;
+    p.negate_q = signbit(scale) != 0;
+    p.causal = causal != 0;
+
+    const Plan plan = plan_for(BH, N, M, bf16, num_splits);
+    const int64_t blocks = plan.kind == Plan::DECODE ? BH * plan.splits : BH * ceil_div(N, 128) * plan.splits;
+    if (blocks > kMaxBlocks) return ATTN_ERR_OVERFLOW;
+    p.splits = plan.splits;
+    p.tiles_per_split = plan.tiles_per_split;
+    if (plan.kind == Plan::SINGLE) {
+        p.tiles_per_split = ceil_div(M, bf16 ? osa::kBf16KeyTile : osa::kF32KeyTile);
+        const hipError_t e = bf16 ? osa::launch_attn_bf16(p, stream) : osa::launch_attn_f32(p, stream);
+        if (e != hipSuccess) {
+            set_detail("attention kernel launch", e);
+            return ATTN_ERR_HIP;
+        }
+        return ATTN_OK;
+    }
+
+    // Split paths: partials in a stream-ordered workspace.
+    const size_t rows = (size_t)BH * (size_t)N;
+    const size_t o_bytes = (size_t)plan.splits * rows * (size_t)d * sizeof(float);
+    const size_t l_bytes = (size_t)plan.splits * rows * sizeof(float);
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, o_bytes + l_bytes, stream);
+    if (e != hipSuccess) {
+        set_detail("hipMallocAsync of the split workspace", e);
+        return ATTN_ERR_HIP;
+    }
+    p.part_o = static_cast<float *>(ws);
+    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(ws) + o_bytes);
+    if (plan.kind == Plan::DECODE)
+        e = osa::launch_attn_decode(p, bf16, stream);
+    else
+        e = bf16 ? osa::launch_attn_bf16(p, stream) : osa::launch_attn_f32(p, stream);
+    if (e == hipSuccess) {
+        e = osa::launch_split_merge(p, bf16, stream);
+        if (e != hipSuccess) set_detail("split merge kernel launch", e);
+    } else {
+        set_detail("split attention kernel launch", e);
+    }
+    const hipError_t ef = hipFreeAsync(ws, stream);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+    if (ef != hipSuccess) {
+        set_detail("hipFreeAsync of the split workspace", ef);
+        return ATTN_ERR_HIP;
+    }
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H, int64_t N,
+             int64_t M, int d, float scale, int causal, int dtype, void *stream) {
+    return run_attn(q, k, v, o, lse, B, H, N, M, d, scale, causal, dtype, 0, stream);
+}
+
+int attn_fwd_splits(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
+                    int64_t N, int64_t M, int d, float scale, int causal, int dtype, int num_splits, void *stream) {
+    return run_attn(q, k, v, o, lse, B, H, N, M, d, scale, causal, dtype, num_splits, stream);
+}
+
+int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stream) {
+    if (rows < 0 || n < 0) return ATTN_ERR_SHAPE;
+    if (rows == 0) return ATTN_OK;
+    if (n < 1) return ATTN_ERR_SHAPE;
+    if (!x || !y) return ATTN_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y)) return ATTN_ERR_ALIGN;
+    if (n > kI32Max || rows > (int64_t(1) << 62) / n) return ATTN_ERR_OVERFLOW;
+    const hipError_t e = osa::launch_online_softmax(x, y, rows, n, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        set_detail("online softmax kernel launch", e);
+        return ATTN_ERR_HIP;
+    }
+    return ATTN_OK;
+}
+
+const char *attn_strerror(int code) {
+    switch (code) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape (negative size, or M < 1 / n < 1 with work to do)";
+    case ATTN_ERR_HEADDIM: return "unsupported head dim (compiled for d = 64 and d = 128)";
+    case ATTN_ERR_DTYPE: return "unsupported dtype (ATTN_F32 or ATTN_BF16)";
+    case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case ATTN_ERR_OVERFLOW: return "sizes exceed the kernels' index range";
+    case ATTN_ERR_HIP: return "HIP launch or allocation failed";
+    case ATTN_ERR_SCALE: return "scale is not finite";
+    case ATTN_ERR_SPLITS: return "num_splits outside [0, ATTN_MAX_SPLITS]";
+    default: return "unknown error code";
+    }
+}
+
+const char *attn_last_error_detail(void) { return g_detail; }
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal launcher interface between the C-ABI front end (attn_api.cpp) and
+// the HIP kernels.  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace osa {
+
+// One attention problem, already validated by the front end.
+struct AttnProblem {
+    const void *q, *k, *v;  // [BH,N,d] / [BH,M,d] / [BH,M,d], dtype elements
+    void *o;                 // [BH,N,d] dtype (unused when writing partials)
+    float *lse;              // [BH,N]          (unused when writing partials)
+    int BH, N, M, d;
+    float c;                 // |scale| * log2(e): scores are kept in base-2 units
+    bool negate_q;           // scale < 0: q's sign is flipped on load so c >= 0
+    bool causal;
+    // Split over keys: split s covers tiles [s*tiles_per_split, (s+1)*tiles_per_split)
+    // of the kernel's key tile size.  splits == 1 writes o and lse directly.
+    int splits;
+    int tiles_per_split;
+    float *part_o;           // [splits,BH,N,d] fp32, normalised partial outputs
+    float *part_lse;         // [splits,BH,N]   fp32, natural-log partial LSE (-inf if empty)
+};
+
+// Key tile sizes (the unit of a split range) of each kernel family.
+constexpr int kBf16KeyTile = 64;
+constexpr int kF32KeyTile = 32;
+constexpr int kDecodeKeyTile = 64;
+constexpr int kDecodeMaxQueries = 4;
+
+hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnProblem &p, hipStream_t stream);
+// Few queries per head (N <= kDecodeMaxQueries), bf16 or fp32 inputs, always
+// writes partials (p.splits >= 1).
+hipError_t launch_attn_decode(const AttnProblem &p, bool bf16, hipStream_t stream);
+// lse = log sum_s e^{part_lse}, o = sum_s e^{part_lse - lse} part_o.
+hipError_t launch_split_merge(const AttnProblem &p, bool bf16, hipStream_t stream);
+
+hipError_t launch_online_softmax(const float *x, float *y, int64_t rows, int64_t n, hipStream_t stream);
+
+}  // namespace osa

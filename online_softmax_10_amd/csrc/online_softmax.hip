@@ -1,0 +1,119 @@
+// Row-wise softmax with the one-pass normaliser, fp32, for gfx950.
+//
+// Pass 1 keeps, per lane, the running max m and running sum s of the
+// elements it visits (m_i = max(m_{i-1}, x_i), s_i = s_{i-1} e^{m_{i-1}-m_i}
+// + e^{x_i - m_i}), a chunk of four elements at a time; the 64 lane states are
+// merged with the same rule (max of the two maxima, each sum rescaled to it).
+// Pass 2 writes y = e^{x - m} / s.  Two reads and one write per element,
+// against three reads and one write for the three-pass safe softmax.
+// Sources: "Online Softmax and Flash Attention" page, section "Online softmax",
+// eq. (3)-(7) and the pass counts in its introduction; "Softmax与Flash-Attention"
+// page, online-softmax derivation.
+//
+// One 64-wide wave per row, four rows per workgroup.  Exponentials are
+// v_exp_f32 on base-2 arguments: e^{x - m} = 2^{x*log2(e) - m*log2(e)}, one FMA.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace osa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float NEG_INF = -__builtin_inff();
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Running state of the recurrence, kept in base-2 units: sh = m * log2(e)
+// (rounded once) is the shift and s = sum_i 2^{x_i log2(e) - sh}.  Every
+// rescale uses differences of stored shifts, so numerator and denominator
+// always share exactly the same shift.
+struct MS {
+    float sh, s;
+};
+
+// Fold the values x[0..CNT) into the state.
+template <int CNT>
+__device__ __forceinline__ void absorb(MS &st, const float *x) {
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < CNT; ++i) mx = fmaxf(mx, x[i]);
+    const float sh_new = fmaxf(st.sh, mx * LOG2E);
+    if (sh_new == NEG_INF) return;  // only -inf seen so far
+    float add = 0.f;
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) add += __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], LOG2E, -sh_new));
+    st.s = st.s * __builtin_amdgcn_exp2f(st.sh - sh_new) + add;
+    st.sh = sh_new;
+}
+
+__device__ __forceinline__ MS merge(MS a, MS b) {
+    const float sh = fmaxf(a.sh, b.sh);
+    if (sh == NEG_INF) return a;
+    const float sa = a.sh == NEG_INF ? 0.f : a.s * __builtin_amdgcn_exp2f(a.sh - sh);
+    const float sb = b.sh == NEG_INF ? 0.f : b.s * __builtin_amdgcn_exp2f(b.sh - sh);
+    return MS{sh, sa + sb};
+}
+
+template <bool VEC>
+__device__ __forceinline__ void softmax_row(const float *xr, float *yr, int64_t n,
+                                            int lane) {
+    MS st{NEG_INF, 0.f};
+    if constexpr (VEC) {
+        const int64_t nv = n >> 2;
+        for (int64_t i = lane; i < nv; i += 64) {
+            const f32x4 v = reinterpret_cast<const f32x4 *>(xr)[i];
+            const float t[4] = {v[0], v[1], v[2], v[3]};
+            absorb<4>(st, t);
+        }
+    } else {
+        for (int64_t i = lane; i < n; i += 64) {
+            const float t[1] = {xr[i]};
+            absorb<1>(st, t);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        MS o{__shfl_xor(st.sh, off, 64), __shfl_xor(st.s, off, 64)};
+        st = merge(st, o);
+    }
+    const float sh = st.sh;
+    const float inv = 1.f / st.s;
+    if constexpr (VEC) {
+        const int64_t nv = n >> 2;
+        for (int64_t i = lane; i < nv; i += 64) {
+            const f32x4 v = reinterpret_cast<const f32x4 *>(xr)[i];
+            f32x4 r;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[j], LOG2E, -sh)) * inv;
+            reinterpret_cast<f32x4 *>(yr)[i] = r;
+        }
+    } else {
+        for (int64_t i = lane; i < n; i += 64) yr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xr[i], LOG2E, -sh)) * inv;
+    }
+}
+
+// Grid-stride over rows, one wave per row.
+template <bool VEC>
+__global__ __launch_bounds__(256) void online_softmax_kernel(const float *x, float *y,
+                                                             int64_t rows, int64_t n) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4)
+        softmax_row<VEC>(x + row * n, y + row * n, n, lane);
+}
+
+}  // namespace
+
+hipError_t launch_online_softmax(const float *x, float *y, int64_t rows, int64_t n, hipStream_t stream) {
+    const int64_t want = (rows + 3) / 4;
+    const dim3 grid((unsigned)(want < 65536 ? want : 65536));
+    if ((n & 3) == 0)
+        hipLaunchKernelGGL((online_softmax_kernel<true>), grid, dim3(256), 0, stream, x, y, rows, n);
+    else
+        hipLaunchKernelGGL((online_softmax_kernel<false>), grid, dim3(256), 0, stream, x, y, rows, n);
+    return hipGetLastError();
+}
+
+}  // namespace osa

@@ -1,0 +1,130 @@
+"""The C-ABI library loads without a GPU, exports every declared symbol, and
+rejects invalid arguments with the documented codes before any HIP call
+(these calls never touch a device; all pointers here are host addresses that
+the library must not dereference)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import online_softmax_10_amd as osa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, HEADDIM, DTYPE, ALIGN, OVERFLOW, HIP, SCALE, SPLITS = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+
+
+def declared_functions():
+    with open(HEADER, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    return osa.lib()
+
+
+@pytest.fixture(scope="module")
+def buf():
+    # 16-byte aligned host scratch; only its address is passed.
+    raw = np.zeros(1024, dtype=np.uint8)
+    base = raw.ctypes.data
+    aligned = (base + 15) & ~15
+    yield aligned
+    del raw
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(osa.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(L, n), f"libattn.so does not export {n}"
+
+
+def test_constants_match_header():
+    with open(HEADER, encoding="utf-8") as f:
+        text = f.read()
+    codes = dict((m[0], int(m[1])) for m in re.findall(r"(ATTN_[A-Z0-9_]+)\s*=\s*(-?\d+)", text))
+    for code, name in osa.ERROR_NAMES.items():
+        assert codes[name] == code
+    assert codes["ATTN_F32"] == osa.ATTN_F32 and codes["ATTN_BF16"] == osa.ATTN_BF16
+    assert int(re.search(r"#define ATTN_MAX_SPLITS (\d+)", text).group(1)) == osa.ATTN_MAX_SPLITS
+
+
+def test_strerror(L):
+    for code in list(osa.ERROR_NAMES) + [12345, -100]:
+        s = L.attn_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert L.attn_strerror(0) == b"success"
+    assert L.attn_last_error_detail() == b""
+
+
+def call(L, buf, B=1, H=1, N=4, M=4, d=64, scale=0.125, causal=0, dtype=1, splits=0,
+         q=None, k=None, v=None, o=None, lse=None):
+    ptr = lambda p: buf if p is None else p
+    return L.attn_fwd_splits(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), B, H, N, M, d, scale, causal, dtype,
+                             splits, None)
+
+
+def test_attn_validation(L, buf):
+    assert call(L, buf, B=-1) == SHAPE
+    assert call(L, buf, N=-3) == SHAPE
+    assert call(L, buf, M=-1) == SHAPE
+    assert call(L, buf, M=0) == SHAPE
+    assert call(L, buf, dtype=2) == DTYPE
+    assert call(L, buf, dtype=-1) == DTYPE
+    for d in (0, 32, 96, 256):
+        assert call(L, buf, d=d) == HEADDIM
+    for s in (float("nan"), float("inf"), float("-inf")):
+        assert call(L, buf, scale=s) == SCALE
+    assert call(L, buf, splits=-1) == SPLITS
+    assert call(L, buf, splits=osa.ATTN_MAX_SPLITS + 1) == SPLITS
+    for name in ("q", "k", "v", "o", "lse"):
+        assert call(L, buf, **{name: 0}) == NULL, name
+        assert call(L, buf, **{name: buf + 4}) == ALIGN, name
+        assert call(L, buf, **{name: buf + 8}) == ALIGN, name
+    assert call(L, buf, N=2**31 // 64) == OVERFLOW
+    assert call(L, buf, M=2**31 // 128, d=128) == OVERFLOW
+    assert call(L, buf, B=2**31) == OVERFLOW
+    assert call(L, buf, B=2**16, H=2**16) == OVERFLOW
+    assert call(L, buf, B=2**13, H=2**10, N=512) == OVERFLOW  # 2^25 workgroups
+
+
+def test_attn_empty_is_noop(L, buf):
+    # B*H*N == 0 returns OK without touching the (null) pointers or a device.
+    for kw in (dict(B=0), dict(H=0), dict(N=0)):
+        assert call(L, buf, q=0, k=0, v=0, o=0, lse=0, **kw) == OK
+    assert L.attn_fwd(None, None, None, None, None, 0, 1, 1, 1, 64, 1.0, 0, 1, None) == OK
+    # validation of the other arguments still applies
+    assert call(L, buf, N=0, d=32) == HEADDIM
+
+
+def test_online_softmax_validation(L, buf):
+    f = L.online_softmax
+    assert f(buf, buf, -1, 3, None) == SHAPE
+    assert f(buf, buf, 1, -3, None) == SHAPE
+    assert f(buf, buf, 2, 0, None) == SHAPE
+    assert f(None, buf, 1, 3, None) == NULL
+    assert f(buf, None, 1, 3, None) == NULL
+    assert f(buf + 4, buf, 1, 3, None) == ALIGN
+    assert f(buf, buf + 8, 1, 3, None) == ALIGN
+    assert f(buf, buf, 1, 2**31, None) == OVERFLOW
+    assert f(buf, buf, 2**40, 2**30, None) == OVERFLOW
+    assert f(None, None, 0, 5, None) == OK
+    assert f(None, None, 0, 0, None) == OK
+
+
+def test_binding_raises_without_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(2, 3)
+    with pytest.raises(ValueError):
+        osa.online_softmax(x)
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        osa.fwd(q, q, q)
