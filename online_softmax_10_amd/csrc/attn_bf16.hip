@@ -51,6 +51,7 @@ constexpr int BR = 32 * NW;      // query rows per workgroup
 constexpr int BC = kBf16KeyTile; // keys per tile
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994531f;
+constexpr float RESCALE_SLACK = 8.f;  // base-2 units: probabilities stay below 2^8
 
 template <int D>
 struct Layout {
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t Vt[D * Lay::VS];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, keeps tile skips scalar
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
@@ -140,20 +141,21 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const int v_kg = tid % Lay::V_GROUPS;  // key group (V_KPT keys) of this thread
     const int v_c8 = tid / Lay::V_GROUPS;  // 8-wide d chunk of this thread
 
+    // Keys past the end of the range are clamped to the last valid key: their
+    // scores are masked to -inf and their probabilities are exactly 0, so the
+    // (finite) duplicated rows contribute nothing, and the loads need no branch.
     auto fetch = [&](int kv0) {
 #pragma unroll
         for (int i = 0; i < Lay::K_LOADS; ++i) {
             const int id = tid + i * NT;
             const int row = id / (D / 8), c8 = id % (D / 8);
-            const int key = kv0 + row;
-            kreg[i] = key < ke ? *reinterpret_cast<const u32x4 *>(kh + (size_t)key * D + c8 * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
+            const int key = min(kv0 + row, ke - 1);
+            kreg[i] = *reinterpret_cast<const u32x4 *>(kh + (size_t)key * D + c8 * 8);
         }
 #pragma unroll
         for (int i = 0; i < Lay::V_KPT; ++i) {
-            const int key = kv0 + Lay::V_KPT * v_kg + i;
-            vreg[i] = key < ke ? *reinterpret_cast<const u32x4 *>(vh + (size_t)key * D + v_c8 * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
+            const int key = min(kv0 + Lay::V_KPT * v_kg + i, ke - 1);
+            vreg[i] = *reinterpret_cast<const u32x4 *>(vh + (size_t)key * D + v_c8 * 8);
         }
     };
     auto stash = [&]() {
@@ -193,19 +195,20 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
         __syncthreads();
         if (t + 1 < ntiles) fetch(kv0 + BC);
 
-        if (CAUSAL && kv0 > wq_lo + 31) continue;  // every key of the tile is after every row of this wave
+        // (A wave whose rows all precede the tile still runs it fully masked:
+        // the workgroup waits at the next barrier anyway, and a skip branch
+        // here makes the compiler copy the accumulators every tile.)
 
         // S^T = K Q^T for two 32-key blocks.
         f32x16 s[2] = {f32x16{}, f32x16{}};
+        const uint16_t *krow = &Ks[perm32(l32) * Lay::KS + 8 * hh];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            const uint16_t *krow = &Ks[(32 * cb + perm32(l32)) * Lay::KS + 8 * hh];
+        for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(krow + 16 * kk);
+            for (int cb = 0; cb < 2; ++cb) {
+                const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(krow + 32 * cb * Lay::KS + 16 * kk);
                 s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], s[cb], 0, 0, 0);
             }
-        }
 
         // Accumulator register r of block cb holds key kv0 + 32*cb + 16*(r/8) + 8*hh + r%8.
         const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > wq_lo);
@@ -226,10 +229,17 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
         mx = xhalf_max(mx);
+        // Lazy rescale: the running shift m_run only moves when the tile max
+        // exceeds it by more than RESCALE_SLACK (base-2 units), so most tiles
+        // need no rescale of l and o~; probabilities then stay below
+        // 2^RESCALE_SLACK.  Any shift gives the same softmax, as long as the
+        // numerator and denominator share it and nothing overflows.
         const float m_tile = mx == NEG_INF ? NEG_INF : mx * c;
-        const float m_new = fmaxf(m_run, m_tile);
+        const bool move = m_tile > m_run + RESCALE_SLACK;
+        const float m_new = move ? m_tile : m_run;
         const float m_use = m_new == NEG_INF ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run - m_use);
+        const float alpha = move ? exp2_fast(m_run - m_use) : 1.f;
+        const bool any_move = __builtin_amdgcn_ballot_w64(move) != 0;
         m_run = m_new;
 
         float lsum = 0.f;
@@ -248,19 +258,20 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
             pop[t4] = __builtin_convertvector(p, bf16x8);
         }
         l_run = alpha * l_run + lsum;
+        if (any_move) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        }
 
         // O^T += V^T P^T
+        const uint16_t *vrow = &Vt[l32 * Lay::VS + 8 * hh];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const uint16_t *vrow = &Vt[(32 * db + l32) * Lay::VS + 8 * hh];
+        for (int t4 = 0; t4 < BC / 16; ++t4)
 #pragma unroll
-            for (int t4 = 0; t4 < BC / 16; ++t4) {
-                const bf16x8 vop = *reinterpret_cast<const bf16x8 *>(vrow + 16 * t4);
+            for (int db = 0; db < D / 32; ++db) {
+                const bf16x8 vop = *reinterpret_cast<const bf16x8 *>(vrow + 32 * db * Lay::VS + 16 * t4);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[t4], oacc[db], 0, 0, 0);
             }
-        }
     }
 
     const float l_tot = xhalf_sum(l_run);

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const void *__restri
     __shared__ float sm_o[NG][NQ][D];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int g = lane / LPK;         // key group within the wave
     const int e0 = (lane % LPK) * EPL; // first d index this lane covers
@@ -122,9 +122,10 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const void *__restri
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             key[u] = base + wave * KPW * U + u * KPW + g;
-            const bool ok = key[u] < ke;
-            kr[u] = ok ? *reinterpret_cast<const u32x4 *>(kh + ((size_t)key[u] * D + e0) * ESZ) : u32x4{0u, 0u, 0u, 0u};
-            vr[u] = ok ? *reinterpret_cast<const u32x4 *>(vh + ((size_t)key[u] * D + e0) * ESZ) : u32x4{0u, 0u, 0u, 0u};
+            // past the range: reload the last valid key (masked below, weight exactly 0)
+            const int kc = min(key[u], ke - 1);
+            kr[u] = *reinterpret_cast<const u32x4 *>(kh + ((size_t)kc * D + e0) * ESZ);
+            vr[u] = *reinterpret_cast<const u32x4 *>(vh + ((size_t)kc * D + e0) * ESZ);
         }
         float kf[U][EPL], vf[U][EPL];
 #pragma unroll
