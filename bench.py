@@ -118,6 +118,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -133,6 +135,15 @@ def main() -> int:
     import online_softmax_10_amd as osa
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": args.steps}), flush=True)
+        return 0
     w = si.WORKLOADS[args.workload]
     err(f"[bench] workload {w}")
     q, k, v = si.make_qkv(w, args.seed)

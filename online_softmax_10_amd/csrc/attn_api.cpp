@@ -3,6 +3,7 @@
 // workspace.  The declarations and their contracts are in include/attn.h.
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -104,7 +105,10 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     p.N = (int)N;
     p.M = (int)M;
     p.d = d;
-    p.c = fabsf(scale) * 1.4426950408889634f;
+    // Scores are kept in base-2 units.  c is at least the smallest normal float
+    // so that a masked score (-inf) times c is -inf, never NaN; for scale = 0
+    // this changes the (uniform) result by less than 2^-100 relative.
+    p.c = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
     p.negate_q = signbit(scale) != 0;
     p.causal = causal != 0;
 

@@ -10,24 +10,31 @@
 // "Softmax与Flash-Attention" page's FlashAttention core idea (tiles of Q, K, V
 // stay on chip, S and P never reach HBM; queries outer, keys inner).
 //
-// Mapping to the chip (all of it specific to this design, not the pages'):
+// Mapping to the chip (specific to this design, not the pages'):
 //  * A workgroup owns BR = 128 query rows of one (batch, head): four 64-wide
-//    waves, 32 rows each.  A wave keeps its 32 query rows in VGPRs as the B
-//    operand of v_mfma_f32_32x32x16_bf16 for the whole key loop.
-//  * Key tiles of BC = 64 keys stream through LDS: K row-major, V transposed
-//    (d-major) so both MFMA operands are single 16-byte LDS reads.  The next
-//    tile is fetched from HBM into registers while the current one is used.
+//    waves, 32 rows each; two workgroups share a compute unit, so each SIMD
+//    runs two waves whose MFMA and VALU phases overlap.  A wave keeps its 32
+//    query rows in VGPRs as the B operand of v_mfma_f32_32x32x16_bf16.
+//  * Key tiles of BC = 64 keys are copied HBM -> LDS by buffer loads with
+//    the LDS-direct path (no staging registers), into two LDS stages: tile
+//    t+1 streams in while tile t is used.  The buffer range check returns
+//    zeros past key M, so ragged tails need no clamping.  Rows are stored in
+//    natural layout with an XOR swizzle of their 16-byte chunks.
 //  * Scores are computed transposed, S^T = K Q^T, so each lane owns one query
-//    (column) and 16 keys per 32x32 block: the row max and row sum are
-//    in-lane plus one exchange between the two wave halves
-//    (v_permlane32_swap).  The K rows fed to the MFMA are permuted (bits 2
-//    and 3 of the row index swapped) so that the accumulator registers that
-//    form the next MFMA's B operand hold 8 consecutive keys: P^T goes from
-//    accumulators to bf16 operand registers with no data movement.
-//  * O^T = V^T P^T keeps one query per lane again, so the per-row rescale
-//    e^{m_old - m_new} and the final 1/l are per-lane scalars.
-//  * Scores stay in base-2 units: c = |scale| * log2(e) is folded into one
-//    FMA before v_exp_f32; a negative scale flips q's sign bit on load.
+//    and 16 keys per 32x32 block: row max and row sum are in-lane plus one
+//    exchange between the wave halves (v_permlane32_swap).  The K rows fed to
+//    the MFMA are permuted (bits 2 and 3 of the row index swapped) so the
+//    accumulator registers forming the next MFMA's B operand hold 8
+//    consecutive keys: P^T goes from accumulators to operands in place.
+//  * O^T = V^T P^T: the V^T operand is read from the natural-layout V tile
+//    with ds_read_b64_tr_b16 (a transposing LDS read), so V is never
+//    transposed in registers; each lane again owns one query, so the rescale
+//    and the final 1/l are per-lane scalars.
+//  * Scores stay in base-2 units: c = |scale| * log2(e) (at least the
+//    smallest normal float, so masked scores of -inf always give exactly 0)
+//    is folded into one FMA before v_exp_f32; a negative scale flips q's sign
+//    bit on load.  The running max only moves when a tile exceeds it by
+//    2^RESCALE_SLACK, so most tiles skip the rescale of l and o~.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,7 +50,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int NW = 4;            // waves per workgroup
 constexpr int NT = 64 * NW;      // threads per workgroup
@@ -51,26 +61,33 @@ constexpr int BR = 32 * NW;      // query rows per workgroup
 constexpr int BC = kBf16KeyTile; // keys per tile
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994531f;
-constexpr float RESCALE_SLACK = 8.f;  // base-2 units: probabilities stay below 2^8
+constexpr float RESCALE_SLACK = 8.f;            // base-2 units: probabilities stay below 2^8
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data
 
 template <int D>
 struct Layout {
-    static constexpr int KS = D + 8;                 // K row stride in LDS (bf16)
-    static constexpr int VS = BC + 8;                // V^T row stride in LDS (bf16)
-    static constexpr int K_LOADS = BC * D / 8 / NT;  // 16-byte K chunks per thread
-    static constexpr int V_KPT = BC * D / 8 / NT;    // keys per thread in the V transpose
-    static constexpr int V_GROUPS = BC / V_KPT;      // key groups across threads
-    static constexpr int LDS_BYTES = (BC * KS + D * VS) * 2;
-    static_assert(K_LOADS * NT * 8 == BC * D, "K tile split");
-    static_assert(V_KPT == 2 || V_KPT == 4, "V transpose width");
+    static constexpr int RB = 2 * D;                 // bytes per K/V row
+    static constexpr int CPR = D / 8;                // 16-byte chunks per row
+    static constexpr int TILE = BC * RB;             // bytes per K (or V) tile
+    static constexpr int LOADS = TILE / 1024 / NW;   // 1 KiB LDS-direct loads per wave per tile
+    static constexpr int ROWS_PER_LOAD = 1024 / RB;
+    static_assert(LOADS * NW * 1024 == TILE, "tile split");
 };
 
-// Row r of a 32-row MFMA A operand reads K row perm32(r): bits 2 and 3 swapped.
-__device__ __forceinline__ int perm32(int r) {
-    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+// Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r).
+// d = 128 (one row per 256-byte bank line): 16 consecutive rows get 16
+// distinct values (K reads: 32 rows, one chunk column), and rows 4m..4m+3
+// move whole 64-byte groups apart (V transposed reads: 4 rows x 64 bytes).
+// d = 64 (two rows per bank line): the same two properties per row parity.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// Reduce across the two 32-lane halves of the wave.
+// Row r of a 32-row MFMA A operand reads K row perm32(r): bits 2 and 3 swapped.
+__device__ __forceinline__ int perm32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
 __device__ __forceinline__ float xhalf_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -82,9 +99,30 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Low (sel=0) or high (sel=1) bf16 halves of a and b packed as (a_half | b_half << 16).
-__device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, int sel) {
-    return __builtin_amdgcn_perm(b, a, sel ? 0x07060302u : 0x05040100u);
+// Wait until at most N LDS-direct loads of this wave are outstanding, then
+// synchronise the workgroup.  The memory clobber keeps LDS accesses on their
+// side of the barrier.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_reads_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One LDS-direct buffer load: each lane's 16 bytes at byte offset voff of the
+// buffer land at LDS address lds_base + 16*lane.  Issued as inline assembly so
+// that the compiler does not track these writes (it would otherwise wait for
+// every outstanding load before each LDS read); completion is ordered
+// explicitly by wait_loads_and_barrier.
+__device__ __forceinline__ void lds_direct_load16(u32x4 rsrc, uint32_t lds_base, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
@@ -94,24 +132,26 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     float *__restrict__ part_lse, int BH, int N, int M, float c, uint32_t qsign, int ntq,
     int splits, int tiles_per_split) {
     using Lay = Layout<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * Lay::KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * Lay::VS];
+    __shared__ __attribute__((aligned(1024))) char lds_k0[Lay::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_k1[Lay::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_v0[Lay::TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_v1[Lay::TILE];
 
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, keeps tile skips scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
-    // Workgroup -> (head, split, query tile); heads vary fastest so that
-    // consecutive workgroups share no K/V and the longest causal tiles go first.
+    // Workgroup -> (head, split, query tile); heads vary fastest and the
+    // longest causal tiles go first.
     const int b = blockIdx.x;
     const int bh = b % BH;
     const int rest = b / BH;
     const int sp = rest % splits;
     const int qt = ntq - 1 - rest / splits;
     const int q0 = qt * BR;
-    const int qrow = q0 + wave * 32 + l32;  // this lane's query row
+    const int qrow = q0 + wave * 32 + l32;
     const int wq_lo = q0 + wave * 32;
 
     const int kb = sp * tiles_per_split * BC;
@@ -120,8 +160,14 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     const int ntiles = ke > kb ? (ke - kb + BC - 1) / BC : 0;
 
     const uint16_t *qh = q + (size_t)bh * N * D;
-    const uint16_t *kh = k + (size_t)bh * M * D;
-    const uint16_t *vh = v + (size_t)bh * M * D;
+    // Buffer descriptors over this head's K and V; reads past key M return 0.
+    const uint64_t kaddr = (uint64_t)(uintptr_t)(k + (size_t)bh * M * D);
+    const uint64_t vaddr = (uint64_t)(uintptr_t)(v + (size_t)bh * M * D);
+    const uint32_t nbytes = (uint32_t)M * Lay::RB;
+    const u32x4 krs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kaddr),
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kaddr >> 32)), nbytes, kBufferWord3};
+    const u32x4 vrs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)vaddr),
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(vaddr >> 32)), nbytes, kBufferWord3};
 
     // Q^T operands: lane (query l32, half hh) holds q[qrow][16*kk + 8*hh .. +8].
     bf16x8 qop[D / 16];
@@ -135,78 +181,68 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
         qop[kk] = __builtin_bit_cast(bf16x8, x);
     }
 
-    // Register staging for the next K/V tile.
-    u32x4 kreg[Lay::K_LOADS];
-    u32x4 vreg[Lay::V_KPT];
-    const int v_kg = tid % Lay::V_GROUPS;  // key group (V_KPT keys) of this thread
-    const int v_c8 = tid / Lay::V_GROUPS;  // 8-wide d chunk of this thread
+    // LDS-direct loads: load i of this wave fills the 1 KiB block (wave*LOADS+i)
+    // of the tile; lane l writes the block's byte 16*l, i.e. row
+    // ROWS_PER_LOAD*(wave*LOADS+i) + l/CPR, physical chunk l%CPR.
+    int ld_off[Lay::LOADS];  // byte offset within a tile of this lane's source chunk
+#pragma unroll
+    for (int i = 0; i < Lay::LOADS; ++i) {
+        const int row = Lay::ROWS_PER_LOAD * (wave * Lay::LOADS + i) + lane / Lay::CPR;
+        const int lc = (lane % Lay::CPR) ^ swz<D>(row);
+        ld_off[i] = row * Lay::RB + lc * 16;
+    }
+    // Offsets are unsigned 32-bit byte offsets within the head (M*d < 2^31 elements).
+    auto issue_tile = [&](int kv0, char *kdst, char *vdst) {
+        const uint32_t base = (uint32_t)kv0 * Lay::RB;
+#pragma unroll
+        for (int i = 0; i < Lay::LOADS; ++i) {
+            const int blk = (wave * Lay::LOADS + i) * 1024;
+            const int off = (int)(base + (uint32_t)ld_off[i]);
+            lds_direct_load16(krs, lds_addr(kdst + blk), off);
+            lds_direct_load16(vrs, lds_addr(vdst + blk), off);
+        }
+    };
 
-    // Keys past the end of the range are clamped to the last valid key: their
-    // scores are masked to -inf and their probabilities are exactly 0, so the
-    // (finite) duplicated rows contribute nothing, and the loads need no branch.
-    auto fetch = [&](int kv0) {
+    // K operand byte offsets (block cb adds 32 rows): row perm32(l32), logical
+    // chunk 2*kk + hh.
+    int k_off[D / 16];
+    {
+        const int row = perm32(l32);
 #pragma unroll
-        for (int i = 0; i < Lay::K_LOADS; ++i) {
-            const int id = tid + i * NT;
-            const int row = id / (D / 8), c8 = id % (D / 8);
-            const int key = min(kv0 + row, ke - 1);
-            kreg[i] = *reinterpret_cast<const u32x4 *>(kh + (size_t)key * D + c8 * 8);
-        }
+        for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = row * Lay::RB + (((2 * kk + hh) ^ swz<D>(row)) * 16);
+    }
+    // V^T operand byte offsets for transposing read r of dv block db (key
+    // chunk t4 adds 16 rows): lane l of 16-lane group G points at key row
+    // 8*(G/2) + 4*r + (l%16)/4 and dv 32*db + 16*(G%2) + 4*(l%4); the read
+    // returns to lane i of the group the 4 keys of that group at dv
+    // 32*db + 16*(G%2) + i.
+    int v_off[2][D / 32];
+    {
+        const int G = lane >> 4, L = lane & 15;
 #pragma unroll
-        for (int i = 0; i < Lay::V_KPT; ++i) {
-            const int key = min(kv0 + Lay::V_KPT * v_kg + i, ke - 1);
-            vreg[i] = *reinterpret_cast<const u32x4 *>(vh + (size_t)key * D + v_c8 * 8);
-        }
-    };
-    auto stash = [&]() {
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int i = 0; i < Lay::K_LOADS; ++i) {
-            const int id = tid + i * NT;
-            const int row = id / (D / 8), c8 = id % (D / 8);
-            *reinterpret_cast<u32x4 *>(&Ks[row * Lay::KS + c8 * 8]) = kreg[i];
-        }
-        // Transpose V_KPT keys x 8 d-values into 8 rows of V^T.
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int dv = v_c8 * 8 + j;
-            if constexpr (Lay::V_KPT == 4) {
-                u32x2 w;
-                w[0] = pack_halves(vreg[0][j >> 1], vreg[1][j >> 1], j & 1);
-                w[1] = pack_halves(vreg[2][j >> 1], vreg[3][j >> 1], j & 1);
-                *reinterpret_cast<u32x2 *>(&Vt[dv * Lay::VS + 4 * v_kg]) = w;
-            } else {
-                *reinterpret_cast<uint32_t *>(&Vt[dv * Lay::VS + 2 * v_kg]) =
-                    pack_halves(vreg[0][j >> 1], vreg[1][j >> 1], j & 1);
+            for (int db = 0; db < D / 32; ++db) {
+                const int row = 8 * (G >> 1) + 4 * r + (L >> 2);
+                const int dv = 32 * db + 16 * (G & 1) + 4 * (L & 3);
+                v_off[r][db] = row * Lay::RB + (((dv >> 3) ^ swz<D>(row)) * 16) + (dv & 7) * 2;
             }
-        }
-    };
+    }
 
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-    float m_run = NEG_INF;  // running max, base-2 units
+    float m_run = NEG_INF;  // running shift (max), base-2 units
     float l_run = 0.f;      // this lane's share of the running sum
 
-    if (ntiles > 0) fetch(kb);
-    for (int t = 0; t < ntiles; ++t) {
-        const int kv0 = kb + t * BC;
-        __syncthreads();  // previous tile fully consumed
-        stash();
-        __syncthreads();
-        if (t + 1 < ntiles) fetch(kv0 + BC);
-
-        // (A wave whose rows all precede the tile still runs it fully masked:
-        // the workgroup waits at the next barrier anyway, and a skip branch
-        // here makes the compiler copy the accumulators every tile.)
-
-        // S^T = K Q^T for two 32-key blocks.
+    auto compute_tile = [&](int kv0, const char *ks, const char *vs) {
+        // S^T = K Q^T for two 32-key blocks, accumulator chains interleaved.
         f32x16 s[2] = {f32x16{}, f32x16{}};
-        const uint16_t *krow = &Ks[perm32(l32) * Lay::KS + 8 * hh];
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
-                const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(krow + 32 * cb * Lay::KS + 16 * kk);
+                const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(ks + cb * 32 * Lay::RB + k_off[kk]);
                 s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], s[cb], 0, 0, 0);
             }
 
@@ -229,12 +265,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
         mx = xhalf_max(mx);
-        // Lazy rescale: the running shift m_run only moves when the tile max
-        // exceeds it by more than RESCALE_SLACK (base-2 units), so most tiles
-        // need no rescale of l and o~; probabilities then stay below
-        // 2^RESCALE_SLACK.  Any shift gives the same softmax, as long as the
-        // numerator and denominator share it and nothing overflows.
-        const float m_tile = mx == NEG_INF ? NEG_INF : mx * c;
+        // Lazy rescale: any shift gives the same softmax as long as numerator
+        // and denominator share it and nothing overflows.
+        const float m_tile = mx * c;  // -inf stays -inf (c > 0)
         const bool move = m_tile > m_run + RESCALE_SLACK;
         const float m_new = move ? m_tile : m_run;
         const float m_use = m_new == NEG_INF ? 0.f : m_new;
@@ -249,11 +282,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
             f32x8 p;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float sv = s[t4 >> 1][8 * (t4 & 1) + i];
-                float e = exp2_fast(__builtin_fmaf(sv, c, -m_use));
-                if (need_mask) e = sv == NEG_INF ? 0.f : e;
-                p[i] = e;
-                lsum += e;
+                p[i] = exp2_fast(__builtin_fmaf(s[t4 >> 1][8 * (t4 & 1) + i], c, -m_use));
+                lsum += p[i];
             }
             pop[t4] = __builtin_convertvector(p, bf16x8);
         }
@@ -263,15 +293,42 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
             for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
         }
 
-        // O^T += V^T P^T
-        const uint16_t *vrow = &Vt[l32 * Lay::VS + 8 * hh];
+        // O^T += V^T P^T; each V^T operand is two transposing reads.
 #pragma unroll
         for (int t4 = 0; t4 < BC / 16; ++t4)
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 vop = *reinterpret_cast<const bf16x8 *>(vrow + 32 * db * Lay::VS + 16 * t4);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[t4], oacc[db], 0, 0, 0);
+                const char *vt = vs + t4 * 16 * Lay::RB;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_off[0][db]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_off[1][db]));
+                const s16x8 w8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w8), pop[t4],
+                                                                   oacc[db], 0, 0, 0);
             }
+    };
+
+    // Two-stage pipeline, unrolled by two so each stage is a distinct LDS array.
+    constexpr int OUT = 2 * Lay::LOADS;  // loads per wave per tile (K and V)
+    if (ntiles > 0) issue_tile(kb, lds_k0, lds_v0);
+    for (int t = 0; t < ntiles; t += 2) {
+        const int kv0 = kb + t * BC;
+        if (t + 1 < ntiles) {
+            issue_tile(kv0 + BC, lds_k1, lds_v1);
+            wait_loads_and_barrier<OUT>();
+        } else {
+            wait_loads_and_barrier<0>();
+        }
+        compute_tile(kv0, lds_k0, lds_v0);
+        lds_reads_done_barrier();
+        if (t + 1 >= ntiles) break;
+        if (t + 2 < ntiles) {
+            issue_tile(kv0 + 2 * BC, lds_k0, lds_v0);
+            wait_loads_and_barrier<OUT>();
+        } else {
+            wait_loads_and_barrier<0>();
+        }
+        compute_tile(kv0 + BC, lds_k1, lds_v1);
+        lds_reads_done_barrier();
     }
 
     const float l_tot = xhalf_sum(l_run);
@@ -287,8 +344,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
             for (int g = 0; g < 4; ++g) {
                 f32x4 x = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
                            oacc[db][4 * g + 3] * inv};
-                *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * g + 4 * hh) =
-                    __builtin_convertvector(x, bf16x4);
+                *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * g + 4 * hh) = __builtin_convertvector(x, bf16x4);
             }
         if (hh == 0) lse[(size_t)bh * N + qrow] = row_lse;
     } else {
