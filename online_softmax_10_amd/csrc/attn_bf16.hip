@@ -107,18 +107,17 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ void lds_reads_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // One LDS-direct buffer load: each lane's 16 bytes at byte offset voff of the
 // buffer land at LDS address lds_base + 16*lane.  Issued as inline assembly so
 // that the compiler does not track these writes (it would otherwise wait for
 // every outstanding load before each LDS read); completion is ordered
-// explicitly by wait_loads_and_barrier.
+// explicitly by wait_loads_and_barrier.  No memory clobber: the loads may be
+// scheduled among the LDS reads of the other stage; they stay on their side of
+// the (volatile) barrier statements.  M0, the LDS base of the load, is a
+// register the compiler reserves and keeps no live value in here.
 __device__ __forceinline__ void lds_direct_load16(u32x4 rsrc, uint32_t lds_base, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_base), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(lds_base), "v"(voff), "s"(rsrc));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -235,16 +234,30 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     float m_run = NEG_INF;  // running shift (max), base-2 units
     float l_run = 0.f;      // this lane's share of the running sum
 
-    auto compute_tile = [&](int kv0, const char *ks, const char *vs) {
+    // Computes the tile at kv0 from stages (ks, vs) and, spread between its
+    // score MFMAs, issues the loads of the next tile (at nkv0, if any) into
+    // the other stages (nks, nvs).
+    auto compute_tile = [&](int kv0, const char *ks, const char *vs, bool has_next, int nkv0, char *nks,
+                            char *nvs) {
         // S^T = K Q^T for two 32-key blocks, accumulator chains interleaved.
         f32x16 s[2] = {f32x16{}, f32x16{}};
+        const uint32_t nbase = (uint32_t)nkv0 * Lay::RB;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
+        for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(ks + cb * 32 * Lay::RB + k_off[kk]);
                 s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], s[cb], 0, 0, 0);
             }
+            constexpr int EVERY = (D / 16) / Lay::LOADS;
+            if (has_next && kk % EVERY == 0) {
+                const int i = kk / EVERY;
+                const int blk = (wave * Lay::LOADS + i) * 1024;
+                const int off = (int)(nbase + (uint32_t)ld_off[i]);
+                lds_direct_load16(krs, lds_addr(nks + blk), off);
+                lds_direct_load16(vrs, lds_addr(nvs + blk), off);
+            }
+        }
 
         // Accumulator register r of block cb holds key kv0 + 32*cb + 16*(r/8) + 8*hh + r%8.
         const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > wq_lo);
@@ -307,28 +320,18 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
             }
     };
 
-    // Two-stage pipeline, unrolled by two so each stage is a distinct LDS array.
-    constexpr int OUT = 2 * Lay::LOADS;  // loads per wave per tile (K and V)
+    // Two LDS stages, one barrier per tile: the wait + barrier at the top of
+    // tile t lands tile t (its loads were issued during tile t-1) and retires
+    // every read of the other stage, which tile t's loads then refill.
+    // Unrolled by two so each stage is a distinct LDS array.
     if (ntiles > 0) issue_tile(kb, lds_k0, lds_v0);
     for (int t = 0; t < ntiles; t += 2) {
         const int kv0 = kb + t * BC;
-        if (t + 1 < ntiles) {
-            issue_tile(kv0 + BC, lds_k1, lds_v1);
-            wait_loads_and_barrier<OUT>();
-        } else {
-            wait_loads_and_barrier<0>();
-        }
-        compute_tile(kv0, lds_k0, lds_v0);
-        lds_reads_done_barrier();
+        wait_loads_and_barrier<0>();
+        compute_tile(kv0, lds_k0, lds_v0, t + 1 < ntiles, kv0 + BC, lds_k1, lds_v1);
         if (t + 1 >= ntiles) break;
-        if (t + 2 < ntiles) {
-            issue_tile(kv0 + 2 * BC, lds_k0, lds_v0);
-            wait_loads_and_barrier<OUT>();
-        } else {
-            wait_loads_and_barrier<0>();
-        }
-        compute_tile(kv0 + BC, lds_k1, lds_v1);
-        lds_reads_done_barrier();
+        wait_loads_and_barrier<0>();
+        compute_tile(kv0 + BC, lds_k1, lds_v1, t + 2 < ntiles, kv0 + 2 * BC, lds_k0, lds_v0);
     }
 
     const float l_tot = xhalf_sum(l_run);
