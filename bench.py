@@ -37,7 +37,8 @@ import seeded_inputs as si  # noqa: E402
 
 PEAKS_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["attn_bf16.hip", "attn_f32.hip", "attn_decode.hip", "attn_api.cpp", "kernels.h"]
+KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16_pp.hip", "attn_bf16_common.h", "attn_f32.hip", "attn_decode.hip",
+                  "attn_api.cpp", "kernels.h"]
 
 
 def err(msg: str) -> None:
@@ -52,14 +53,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it matches the source."""
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it covers this
+    kernel and matches the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("kernel") != kernel:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -188,6 +190,7 @@ def main() -> int:
     err(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us), "
         f"{value:.1f} TFLOP/s")
 
+    kernel, splits = osa.plan(w.B, w.H, w.N, w.M, w.d, w.dtype)
     achieved = w.flops / (launch_ms * 1e-3) / 1e12
     peak = PEAKS_TFLOPS[w.dtype]
     roofline = {
@@ -196,8 +199,9 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": load_traffic(w.name),
-        "kernel": "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel",
+        "traffic": load_traffic(w.name, kernel) if splits == 1 else None,
+        "kernel": kernel,
+        "splits": splits,
         "launch_us": round(launch_ms * 1e3, 2),
         "algorithmic_bytes": algorithmic_bytes(w),
         "hbm_gbs_algorithmic": round(algorithmic_bytes(w) / (launch_ms * 1e-3) / 1e9, 1),

@@ -137,6 +137,21 @@ int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stre
 /* Static, human-readable text for a return code (never NULL). */
 const char *attn_strerror(int code);
 
+/*
+ * attn_fwd_plan -- the work decomposition attn_fwd_splits would use, without
+ * launching anything (host only; needs no GPU).
+ *
+ * Returns the name of the kernel that computes the attention itself (one of
+ * "attn_fwd_bf16_pp_kernel", "attn_fwd_bf16_kernel", "attn_fwd_f32_kernel",
+ * "attn_decode_kernel"; a static string, not to be freed) and stores in
+ * *splits (if splits is not NULL) the number of key splits: 1 for a single
+ * pass, >= 2 when the kernel writes partials that the merge kernel combines.
+ * Returns NULL (and *splits = 0) for arguments attn_fwd_splits would reject
+ * or for which it has nothing to compute (B, H or N zero).
+ */
+const char *attn_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int d, int dtype, int num_splits,
+                          int *splits);
+
 /* Detail of the last ATTN_ERR_HIP on the calling thread ("" if none). */
 const char *attn_last_error_detail(void);
 

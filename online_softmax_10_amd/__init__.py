@@ -15,7 +15,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_splits", "online_softmax", "lib", "LIB_PATH", "AttnError",
+__all__ = ["fwd", "fwd_splits", "online_softmax", "plan", "lib", "LIB_PATH", "AttnError",
            "ATTN_F32", "ATTN_BF16", "ATTN_MAX_SPLITS", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -26,7 +26,8 @@ ATTN_MAX_SPLITS = 256
 ERROR_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
                -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_OVERFLOW", -7: "ATTN_ERR_HIP",
                -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_SPLITS"}
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "online_softmax", "attn_strerror", "attn_last_error_detail")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "online_softmax", "attn_fwd_plan", "attn_strerror",
+                    "attn_last_error_detail")
 
 _lib = None
 
@@ -62,13 +63,20 @@ def lib() -> ctypes.CDLL:
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_error_detail.argtypes = []
         L.attn_last_error_detail.restype = ctypes.c_char_p
+        L.attn_fwd_plan.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_int)]
+        L.attn_fwd_plan.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
 
 def _stream_handle(device):
+    """The raw HIP stream of torch's current stream on ``device``."""
     import torch
 
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return ctypes.c_void_p(raw(device.index if device.index is not None else torch.cuda.current_device()))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -80,6 +88,12 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.float32:
         return ATTN_F32
     raise TypeError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
+
+
+def _check_output(name, t, shape, dtype, device):
+    if tuple(t.shape) != shape or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} on {device}; "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
 def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None):
@@ -104,10 +118,16 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
     if out is None:
         out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    else:
+        _check_output("out", out, (B, H, N, d), q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_output("lse", lse, (B, H, N), torch.float32, q.device)
     rc = lib().attn_fwd_splits(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                B, H, N, M, d, float(scale), int(bool(causal)), code, int(num_splits),
                                _stream_handle(q.device))
@@ -121,6 +141,20 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
     return fwd_splits(q, k, v, scale=scale, causal=causal, num_splits=0, out=out, lse=lse)
 
 
+def plan(B, H, N, M, d, dtype="bf16", num_splits=0):
+    """(kernel name, split count) that fwd_splits would use for these sizes.
+
+    Host-side query of the library's work decomposition; launches nothing.
+    Raises ValueError for sizes the library rejects or with nothing to compute.
+    """
+    code = {"bf16": ATTN_BF16, "f32": ATTN_F32}[dtype]
+    splits = ctypes.c_int(0)
+    name = lib().attn_fwd_plan(B, H, N, M, d, code, num_splits, ctypes.byref(splits))
+    if name is None:
+        raise ValueError(f"no plan for B={B} H={H} N={N} M={M} d={d} {dtype} num_splits={num_splits}")
+    return name.decode(), splits.value
+
+
 def online_softmax(x, out=None):
     """Row-wise softmax of a contiguous float32 GPU tensor over its last axis."""
     import torch
@@ -131,6 +165,8 @@ def online_softmax(x, out=None):
     rows = x.numel() // n if n > 0 else 0
     if out is None:
         out = torch.empty_like(x)
+    else:
+        _check_output("out", out, tuple(x.shape), torch.float32, x.device)
     rc = lib().online_softmax(x.data_ptr(), out.data_ptr(), rows, n, _stream_handle(x.device))
     if rc != 0:
         raise AttnError(rc, "online_softmax")

@@ -87,6 +87,30 @@ int validate_attn(const void *q, const void *k, const void *v, const void *o, co
     return ATTN_OK;
 }
 
+// The kernel that carries the attention itself for a plan (the split paths
+// add the merge kernel).
+enum class MainKernel { F32, BF16_4W, BF16_8W, DECODE };
+
+MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16) {
+    if (plan.kind == Plan::DECODE) return MainKernel::DECODE;
+    if (!bf16) return MainKernel::F32;
+    // The eight-wave kernel shares each K/V tile among 256 rows; use it for
+    // single-pass problems whose 256-row tiles alone give every compute unit
+    // a workgroup.
+    if (plan.kind == Plan::SINGLE && BH * ceil_div(N, osa::kBf16PingPongRows) >= 256) return MainKernel::BF16_8W;
+    return MainKernel::BF16_4W;
+}
+
+const char *main_kernel_name(MainKernel k) {
+    switch (k) {
+    case MainKernel::F32: return "attn_fwd_f32_kernel";
+    case MainKernel::BF16_4W: return "attn_fwd_bf16_kernel";
+    case MainKernel::BF16_8W: return "attn_fwd_bf16_pp_kernel";
+    case MainKernel::DECODE: return "attn_decode_kernel";
+    }
+    return "";
+}
+
 int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H, int64_t N,
              int64_t M, int d, float scale, int causal, int dtype, int num_splits, void *stream_v) {
     const int rc = validate_attn(q, k, v, o, lse, B, H, N, M, d, scale, dtype, num_splits);
@@ -115,11 +139,14 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     const Plan plan = plan_for(BH, N, M, bf16, num_splits);
     const int64_t blocks = plan.kind == Plan::DECODE ? BH * plan.splits : BH * ceil_div(N, 128) * plan.splits;
     if (blocks > kMaxBlocks) return ATTN_ERR_OVERFLOW;
+    const MainKernel kernel = main_kernel(plan, BH, N, bf16);
     p.splits = plan.splits;
     p.tiles_per_split = plan.tiles_per_split;
     if (plan.kind == Plan::SINGLE) {
         p.tiles_per_split = ceil_div(M, bf16 ? osa::kBf16KeyTile : osa::kF32KeyTile);
-        const hipError_t e = bf16 ? osa::launch_attn_bf16(p, stream) : osa::launch_attn_f32(p, stream);
+        const hipError_t e = kernel == MainKernel::F32       ? osa::launch_attn_f32(p, stream)
+                             : kernel == MainKernel::BF16_8W ? osa::launch_attn_bf16_pp(p, stream)
+                                                             : osa::launch_attn_bf16(p, stream);
         if (e != hipSuccess) {
             set_detail("attention kernel launch", e);
             return ATTN_ERR_HIP;
@@ -139,10 +166,10 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     }
     p.part_o = static_cast<float *>(ws);
     p.part_lse = reinterpret_cast<float *>(static_cast<char *>(ws) + o_bytes);
-    if (plan.kind == Plan::DECODE)
+    if (kernel == MainKernel::DECODE)
         e = osa::launch_attn_decode(p, bf16, stream);
     else
-        e = bf16 ? osa::launch_attn_bf16(p, stream) : osa::launch_attn_f32(p, stream);
+        e = kernel == MainKernel::BF16_4W ? osa::launch_attn_bf16(p, stream) : osa::launch_attn_f32(p, stream);
     if (e == hipSuccess) {
         e = osa::launch_split_merge(p, bf16, stream);
         if (e != hipSuccess) set_detail("split merge kernel launch", e);
@@ -185,6 +212,20 @@ int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stre
         return ATTN_ERR_HIP;
     }
     return ATTN_OK;
+}
+
+const char *attn_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int d, int dtype, int num_splits,
+                          int *splits) {
+    if (splits) *splits = 0;
+    if (B < 1 || H < 1 || N < 1 || M < 1) return nullptr;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return nullptr;
+    if (d != 64 && d != 128) return nullptr;
+    if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return nullptr;
+    if (B > kI32Max || H > kI32Max || B * H > kI32Max || N > kI32Max / d || M > kI32Max / d) return nullptr;
+    const bool bf16 = dtype == ATTN_BF16;
+    const Plan plan = plan_for(B * H, N, M, bf16, num_splits);
+    if (splits) *splits = plan.splits;
+    return main_kernel_name(main_kernel(plan, B * H, N, bf16));
 }
 
 const char *attn_strerror(int code) {

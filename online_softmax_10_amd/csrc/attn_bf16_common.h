@@ -1,0 +1,311 @@
+// Shared device code of the bf16 attention kernels for gfx950: operand
+// layouts, LDS swizzle, LDS-direct loads and the per-wave tile math of the
+// online-softmax recurrence (scores, running max / sum with lazy rescale,
+// probabilities, P.V, epilogue).
+//
+// Recurrence: per query row a running max m and running exponential sum l;
+// each new key block rescales l and the unnormalised accumulator o~ by
+// e^{m_old - m_new} and adds the block's terms; finally o = o~ / l and
+// LSE = m + log l.  Sources: "从原始Softmax到在线Softmax" page, online softmax
+// derivation (m, l, o~ recurrences) and LSE definition; "Online Softmax and
+// Flash Attention" page, eq. (8) and the fused loop of eq. (20)-(22).
+//
+// One wave owns 32 query rows.  Scores are computed transposed,
+// S^T = K Q^T on v_mfma_f32_32x32x16_bf16, so each lane owns one query and 16
+// keys per 32x32 block: row max and row sum are in-lane plus one exchange
+// between the wave halves (v_permlane32_swap).  The K rows fed to the MFMA are
+// permuted (bits 2 and 3 of the row index swapped) so the accumulator
+// registers forming the next MFMA's B operand hold 8 consecutive keys: P^T
+// goes from accumulators to operands in place.  O^T = V^T P^T takes its V^T
+// operand from ds_read_b64_tr_b16 (a transposing LDS read) on the
+// natural-layout V tile, so the rescale and the final 1/l are per-lane
+// scalars.  Scores stay in base-2 units: c = |scale| * log2(e) (at least the
+// smallest normal float, so masked scores of -inf give exactly 0) is folded
+// into one FMA before v_exp_f32; a negative scale flips q's sign bit on load.
+// The shift (running max) only moves when a tile's max exceeds it by a
+// slack, so most tiles skip the rescale of l and o~.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace osa {
+namespace bf16 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int BC = kBf16KeyTile;  // keys per tile
+constexpr float NEG_INF = -__builtin_inff();
+constexpr float LN2 = 0.69314718055994531f;
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data
+
+template <int D>
+struct Tile {
+    static constexpr int RB = 2 * D;        // bytes per K/V row
+    static constexpr int CPR = D / 8;       // 16-byte chunks per row
+    static constexpr int BYTES = BC * RB;   // bytes per K (or V) tile
+    static constexpr int ROWS_PER_LOAD = 1024 / RB;
+    static constexpr int LOADS = BYTES / 1024;  // 1 KiB LDS-direct loads per tile
+};
+
+// Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r).
+// d = 128 (one row per 256-byte bank line): 16 consecutive rows get 16
+// distinct values (K reads: 32 rows, one chunk column), and rows 4m..4m+3
+// move whole 64-byte groups apart (V transposed reads: 4 rows x 64 bytes).
+// d = 64 (two rows per bank line): the same two properties per row parity.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Row r of a 32-row MFMA A operand reads K row perm32(r): bits 2 and 3 swapped.
+__device__ __forceinline__ int perm32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ __forceinline__ float xhalf_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wait until at most N LDS-direct loads of this wave are outstanding, then
+// synchronise the workgroup.  The memory clobber keeps LDS accesses on their
+// side of the barrier.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One LDS-direct buffer load: each lane's 16 bytes at byte offset voff of the
+// buffer land at LDS address lds_base + 16*lane.  Issued as inline assembly so
+// that the compiler does not track these writes (it would otherwise wait for
+// every outstanding load before each LDS read); completion is ordered
+// explicitly by wait_loads_and_barrier.  No memory clobber: the loads may be
+// scheduled among the LDS reads of other stages; they stay on their side of
+// the (volatile) barrier statements.  M0, the LDS base of the load, is a
+// register the compiler reserves and keeps no live value in here.
+__device__ __forceinline__ void lds_direct_load16(u32x4 rsrc, uint32_t lds_base, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(lds_base), "v"(voff), "s"(rsrc));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Raw buffer descriptor over nbytes at p (wave-uniform); loads past nbytes return 0.
+__device__ __forceinline__ u32x4 make_rsrc(const void *p, uint32_t nbytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)), nbytes, kBufferWord3};
+}
+
+// Copies of one K (or V) tile into LDS are split into Tile::LOADS loads of
+// 1 KiB; load i covers rows ROWS_PER_LOAD*i .. and lane l writes the block's
+// byte 16*l, i.e. row ROWS_PER_LOAD*i + l/CPR, physical chunk l%CPR.  Returns
+// the byte offset, within a tile, of the source chunk of this lane.
+template <int D>
+__device__ __forceinline__ int load_src_offset(int i, int lane) {
+    using T = Tile<D>;
+    const int row = T::ROWS_PER_LOAD * i + lane / T::CPR;
+    const int lc = (lane % T::CPR) ^ swz<D>(row);
+    return row * T::RB + lc * 16;
+}
+
+// The per-wave state and tile math for 32 query rows.
+template <int D, bool CAUSAL>
+struct WaveTile {
+    using T = Tile<D>;
+    bf16x8 qop[D / 16];   // Q^T operand: lane (query l32, half hh) holds q[row][16*kk + 8*hh .. +8]
+    f32x16 oacc[D / 32];  // O^T accumulator: register r of block db is d index 32*db + 8*(r/4) + 4*hh + r%4
+    float m_run;          // running shift (max), base-2 units
+    float l_run;          // this lane's share of the running sum
+    int k_off[D / 16];    // K operand byte offsets (block cb adds 32 rows)
+    int v_off[2][D / 32]; // V^T operand byte offsets (key chunk t4 adds 16 rows)
+    int l32, hh, qrow, wq_lo;
+    float c;
+
+    __device__ __forceinline__ void init(const uint16_t *qh, int N, int row0, int lane, float c_, uint32_t qsign) {
+        l32 = lane & 31;
+        hh = lane >> 5;
+        wq_lo = row0;
+        qrow = row0 + l32;
+        c = c_;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (qrow < N) {
+                x = *reinterpret_cast<const u32x4 *>(qh + (size_t)qrow * D + 16 * kk + 8 * hh);
+                x ^= qsign;
+            }
+            qop[kk] = __builtin_bit_cast(bf16x8, x);
+        }
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+        m_run = NEG_INF;
+        l_run = 0.f;
+        {
+            const int row = perm32(l32);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = row * T::RB + (((2 * kk + hh) ^ swz<D>(row)) * 16);
+        }
+        // Transposing read r of dv block db: lane l of 16-lane group G points at
+        // key row 8*(G/2) + 4*r + (l%16)/4 and dv 32*db + 16*(G%2) + 4*(l%4); the
+        // read returns to lane i of the group the 4 keys of that group at dv
+        // 32*db + 16*(G%2) + i.
+        const int G = lane >> 4, L = lane & 15;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const int row = 8 * (G >> 1) + 4 * r + (L >> 2);
+                const int dv = 32 * db + 16 * (G & 1) + 4 * (L & 3);
+                v_off[r][db] = row * T::RB + (((dv >> 3) ^ swz<D>(row)) * 16) + (dv & 7) * 2;
+            }
+    }
+
+    // One MFMA step kk of S^T = K Q^T for both 32-key blocks.
+    __device__ __forceinline__ void score_step(const char *ks, int kk, f32x16 (&s)[2]) const {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(ks + cb * 32 * T::RB + k_off[kk]);
+            s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], s[cb], 0, 0, 0);
+        }
+    }
+
+    // Masked scores become -inf (then P is exactly 0).
+    __device__ __forceinline__ void mask(int kv0, int ke, f32x16 (&s)[2]) const {
+        // Accumulator register r of block cb holds key kv0 + 32*cb + 16*(r/8) + 8*hh + r%8.
+        const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > wq_lo);
+        if (need_mask) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + 32 * cb + 16 * (r >> 3) + 8 * hh + (r & 7);
+                    const bool ok = key < ke && (!CAUSAL || key <= qrow);
+                    s[cb][r] = ok ? s[cb][r] : NEG_INF;
+                }
+        }
+    }
+
+    // P = 2^(c*s - m) for shift m, rounded to bf16 as the operands of P.V;
+    // returns their sum in fp32 (v_dot2c_f32_bf16 against (1,1)).  l sums the
+    // same rounded values, so o = o~/l is a weighted mean with consistent
+    // weights: with a peaked softmax the rounding of the dominant weights
+    // cancels.
+    __device__ __forceinline__ float probs(const f32x16 (&s)[2], float m, bf16x8 (&pop)[BC / 16]) const {
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float lsum[2] = {0.f, 0.f};  // two chains of v_dot2c
+#pragma unroll
+        for (int t4 = 0; t4 < BC / 16; ++t4) {
+            f32x8 p;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) p[i] = exp2_fast(__builtin_fmaf(s[t4 >> 1][8 * (t4 & 1) + i], c, -m));
+            pop[t4] = __builtin_convertvector(p, bf16x8);
+            float &acc = lsum[t4 & 1];
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop[t4], pop[t4], 0, 1), ones, acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop[t4], pop[t4], 2, 3), ones, acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop[t4], pop[t4], 4, 5), ones, acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop[t4], pop[t4], 6, 7), ones, acc, false);
+        }
+        return lsum[0] + lsum[1];
+    }
+
+    // One online-softmax step on the (masked) scores of a tile: the tile's row
+    // max, a new shift only when that max exceeds the current one by more
+    // than RESCALE_SLACK (base-2 units), then the rescale of l and o~ by
+    // 2^(m_old - m_new) (skipped by the whole wave when no row moved) and the
+    // tile's probabilities.  Any shift gives the same softmax as long as
+    // numerator and denominator share it and nothing overflows; with the
+    // slack, probabilities stay below 2^RESCALE_SLACK.
+    __device__ __forceinline__ void softmax(f32x16 (&s)[2], bf16x8 (&pop)[BC / 16]) {
+        constexpr float RESCALE_SLACK = 8.f;
+        float mx = NEG_INF;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
+        mx = xhalf_max(mx);
+        const float m_tile = mx * c;  // -inf stays -inf (c > 0)
+        const bool move = m_tile > m_run + RESCALE_SLACK;
+        const float m_new = move ? m_tile : m_run;
+        const float m_use = m_new == NEG_INF ? 0.f : m_new;  // fully masked so far: p = 0
+        const float alpha = move ? exp2_fast(m_run - m_use) : 1.f;  // 0 when m_run = -inf
+        const bool any_move = __builtin_amdgcn_ballot_w64(move) != 0;
+        m_run = m_new;
+        const float lsum = probs(s, m_use, pop);
+        l_run = alpha * l_run + lsum;
+        if (any_move) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        }
+    }
+
+    // O^T += V^T P^T; each V^T operand is two transposing reads.
+    __device__ __forceinline__ void pv(const char *vs, const bf16x8 (&pop)[BC / 16]) {
+#pragma unroll
+        for (int t4 = 0; t4 < BC / 16; ++t4)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const char *vt = vs + t4 * 16 * T::RB;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_off[0][db]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_off[1][db]));
+                const s16x8 w8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w8), pop[t4],
+                                                                   oacc[db], 0, 0, 0);
+            }
+    }
+
+    // Final o = o~ / l and LSE; bf16 output or fp32 split partial.
+    template <bool SPLIT>
+    __device__ __forceinline__ void store(int N, uint16_t *o_head, float *lse_head, float *part_o_rows,
+                                          float *part_lse_rows) {
+        const float l_tot = xhalf_sum(l_run);
+        if (qrow >= N) return;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float row_lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2 : NEG_INF;
+        if constexpr (!SPLIT) {
+            uint16_t *orow = o_head + (size_t)qrow * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 x = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                               oacc[db][4 * g + 3] * inv};
+                    *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * g + 4 * hh) = __builtin_convertvector(x, bf16x4);
+                }
+            if (hh == 0) lse_head[qrow] = row_lse;
+        } else {
+            float *orow = part_o_rows + (size_t)qrow * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 x = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                               oacc[db][4 * g + 3] * inv};
+                    *reinterpret_cast<f32x4 *>(orow + 32 * db + 8 * g + 4 * hh) = x;
+                }
+            if (hh == 0) part_lse_rows[qrow] = row_lse;
+        }
+    }
+};
+
+}  // namespace bf16
+}  // namespace osa

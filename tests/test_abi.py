@@ -128,3 +128,33 @@ def test_binding_raises_without_gpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         osa.fwd(q, q, q)
+
+
+def test_plan_kernel_choice():
+    # Host-only query of the decomposition: the five workload shapes and the
+    # regimes between them.
+    assert osa.plan(2, 16, 4096, 4096, 128) == ("attn_fwd_bf16_pp_kernel", 1)
+    assert osa.plan(1, 8, 16384, 16384, 128) == ("attn_fwd_bf16_pp_kernel", 1)
+    assert osa.plan(4, 8, 1024, 1024, 64) == ("attn_fwd_bf16_kernel", 1)
+    name, s = osa.plan(32, 32, 1, 8192, 128)
+    assert name == "attn_decode_kernel" and 1 <= s <= osa.ATTN_MAX_SPLITS
+    assert osa.plan(1, 1, 256, 256, 64, "f32")[0] == "attn_fwd_f32_kernel"
+    # Few query tiles and a long key range: split partials, merged afterwards.
+    name, s = osa.plan(1, 1, 100, 5000, 64)
+    assert name == "attn_fwd_bf16_kernel" and s > 1
+    # An explicit single pass on a small problem takes the four-wave kernel;
+    # the eight-wave kernel never writes partials.
+    assert osa.plan(1, 1, 100, 5000, 64, num_splits=1) == ("attn_fwd_bf16_kernel", 1)
+    assert osa.plan(2, 16, 4096, 4096, 128, num_splits=4) == ("attn_fwd_bf16_kernel", 4)
+    assert osa.plan(1, 1, 4, 8192, 128, num_splits=8) == ("attn_decode_kernel", 8)
+
+
+def test_plan_rejects_like_attn_fwd(L):
+    splits = ctypes.c_int(7)
+    for args in ((0, 1, 4, 4, 64, 1, 0), (1, 1, 0, 4, 64, 1, 0), (1, 1, 4, 0, 64, 1, 0), (1, 1, 4, 4, 96, 1, 0),
+                 (1, 1, 4, 4, 64, 3, 0), (1, 1, 4, 4, 64, 1, -1), (1, 1, 4, 4, 64, 1, osa.ATTN_MAX_SPLITS + 1),
+                 (1, 1, 2**31 // 64, 4, 64, 1, 0)):
+        splits.value = 7
+        assert L.attn_fwd_plan(*args, ctypes.byref(splits)) is None, args
+        assert splits.value == 0
+    assert L.attn_fwd_plan(1, 1, 4, 4, 64, 1, 0, None) is not None

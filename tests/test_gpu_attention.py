@@ -180,3 +180,51 @@ def test_empty_batch_is_noop():
     o, lse = osa.fwd(q, k, k)
     torch.cuda.synchronize()
     assert o.shape == (2, 3, 0, 64) and lse.shape == (2, 3, 0)
+
+
+def test_binding_rejects_bad_outputs():
+    # Caller-supplied outputs are checked before anything is launched.
+    import torch
+
+    import online_softmax_10_amd as osa
+
+    log("[gpu] binding output checks")
+    q = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda")
+    good_o = torch.empty_like(q)
+    good_l = torch.empty((1, 2, 8), dtype=torch.float32, device="cuda")
+    bad_o = [torch.empty((1, 2, 7, 64), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((1, 2, 8, 64), dtype=torch.float32, device="cuda"),
+             torch.empty((1, 2, 64, 8), dtype=torch.bfloat16, device="cuda").transpose(2, 3),
+             torch.empty((1, 2, 8, 64), dtype=torch.bfloat16)]
+    for o in bad_o:
+        with pytest.raises(ValueError):
+            osa.fwd(q, q, q, out=o, lse=good_l)
+    for l in (torch.empty((1, 2, 9), dtype=torch.float32, device="cuda"),
+              torch.empty((1, 2, 8), dtype=torch.bfloat16, device="cuda")):
+        with pytest.raises(ValueError):
+            osa.fwd(q, q, q, out=good_o, lse=l)
+    x = torch.zeros((3, 5), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        osa.online_softmax(x, out=torch.empty((3, 4), dtype=torch.float32, device="cuda"))
+    o, l = osa.fwd(q, q, q, out=good_o, lse=good_l)
+    torch.cuda.synchronize()
+    assert o is good_o and l is good_l
+
+
+# ------------------------------------------------------------------ the eight-wave kernel
+
+# Shapes with at least 256 workgroups of 256 query rows, so the library runs
+# the eight-wave kernel; ragged query and key counts, both head dims.
+PINGPONG = [
+    si.Workload("pp", 1, 256, 256, 300, 128, "bf16", True, "normal"),
+    si.Workload("pp", 1, 256, 256, 300, 128, "bf16", False, "normal"),
+    si.Workload("pp", 2, 64, 257, 513, 64, "bf16", True, "normal"),
+    si.Workload("pp", 1, 128, 384, 200, 128, "bf16", True, "normal_qk3"),
+    si.Workload("pp", 1, 256, 200, 1, 64, "bf16", False, "normal"),
+]
+
+
+@pytest.mark.parametrize("w", PINGPONG, ids=[f"{w.B}x{w.H}x{w.N}x{w.M}d{w.d}{'c' if w.causal else ''}{w.dist}"
+                                             for w in PINGPONG])
+def test_eight_wave_kernel_shapes(w):
+    check_full(w, 21)
