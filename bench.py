@@ -37,7 +37,7 @@ import seeded_inputs as si  # noqa: E402
 
 PEAKS_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16_pp.hip", "attn_bf16_common.h", "attn_f32.hip", "attn_decode.hip",
+KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16_common.h", "attn_f32.hip", "attn_decode.hip",
                   "attn_api.cpp", "kernels.h"]
 
 

@@ -97,7 +97,7 @@ MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16) {
     // The eight-wave kernel shares each K/V tile among 256 rows; use it for
     // single-pass problems whose 256-row tiles alone give every compute unit
     // a workgroup.
-    if (plan.kind == Plan::SINGLE && BH * ceil_div(N, osa::kBf16PingPongRows) >= 256) return MainKernel::BF16_8W;
+    if (plan.kind == Plan::SINGLE && BH * ceil_div(N, osa::kBf16WideRows) >= 256) return MainKernel::BF16_8W;
     return MainKernel::BF16_4W;
 }
 
@@ -105,7 +105,7 @@ const char *main_kernel_name(MainKernel k) {
     switch (k) {
     case MainKernel::F32: return "attn_fwd_f32_kernel";
     case MainKernel::BF16_4W: return "attn_fwd_bf16_kernel";
-    case MainKernel::BF16_8W: return "attn_fwd_bf16_pp_kernel";
+    case MainKernel::BF16_8W: return "attn_fwd_bf16_w8_kernel";
     case MainKernel::DECODE: return "attn_decode_kernel";
     }
     return "";
@@ -145,7 +145,7 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     if (plan.kind == Plan::SINGLE) {
         p.tiles_per_split = ceil_div(M, bf16 ? osa::kBf16KeyTile : osa::kF32KeyTile);
         const hipError_t e = kernel == MainKernel::F32       ? osa::launch_attn_f32(p, stream)
-                             : kernel == MainKernel::BF16_8W ? osa::launch_attn_bf16_pp(p, stream)
+                             : kernel == MainKernel::BF16_8W ? osa::launch_attn_bf16_w8(p, stream)
                                                              : osa::launch_attn_bf16(p, stream);
         if (e != hipSuccess) {
             set_detail("attention kernel launch", e);

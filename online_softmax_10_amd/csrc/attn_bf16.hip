@@ -1,23 +1,40 @@
-// Fused attention forward, bf16 inputs, fp32 accumulation, for gfx950 (CDNA4):
-// the four-wave kernel (128 query rows per workgroup, two workgroups per CU).
-// Used for problems with too few 256-row query tiles to fill the chip with
-// the eight-wave kernel (attn_bf16_pp.hip), and for split partials.
+// Fused attention forward, bf16 inputs, fp32 accumulation, for gfx950 (CDNA4).
 //
-// Method and per-wave tile math: attn_bf16_common.h (online softmax
-// recurrence; "从原始Softmax到在线Softmax" page, online softmax derivation and
-// LSE; "Online Softmax and Flash Attention" page, eq. (8)).  The
-// FlashAttention idea of keeping Q, K, V tiles on chip so S and P never reach
-// HBM ("Softmax与Flash-Attention" page, FlashAttention core idea) with the
+// Method and per-wave pieces: attn_bf16_common.h (online softmax recurrence;
+// "从原始Softmax到在线Softmax" page, online softmax derivation and LSE; "Online
+// Softmax and Flash Attention" page, eq. (8)).  The FlashAttention idea of
+// keeping the Q, K, V tiles on chip so S and P never reach HBM
+// ("Softmax与Flash-Attention" page, FlashAttention core idea), with the
 // query-outer loop order of its v2 section.
 //
-// Mapping: four 64-wide waves own 32 rows each.  Key tiles of 64 keys go
-// HBM -> LDS by LDS-direct buffer loads into two stages; one wait + barrier
-// at the top of tile t lands tile t and retires every read of the other
-// stage, and tile t+1's loads are spread between tile t's score MFMAs.  The
-// buffer range check returns zeros past key M.
+// One kernel body, two widths:
+//   attn_fwd_bf16_kernel     4 waves, 128 query rows per workgroup, two
+//                            workgroups per CU (small problems, split partials);
+//   attn_fwd_bf16_w8_kernel  8 waves, 256 query rows per workgroup, one per CU
+//                            (problems whose 256-row tiles fill the chip), so a
+//                            K/V tile crosses L2 -> LDS once per 256 rows.
+// Either way each SIMD runs two waves.
+//
+// Software pipeline.  Iteration j of a wave's key loop, with the scores
+// S(j) of tile j already in registers:
+//   - one wait + barrier: K(j+1) and V(j) have landed in LDS, and every wave
+//     is done with the stages the iteration's loads overwrite;
+//   - the 16 score MFMAs of S(j+1) = K(j+1) Q^T, each followed by the K
+//     operand read two MFMAs ahead and by the softmax work of two scores of
+//     tile j (FMA, exp2, bf16 pack, dot2 into the sum), so the matrix cores
+//     and the VALU work side by side; K(j+2) and V(j+1) are loaded between;
+//   - the rare exact-shift path (attn_bf16_common.h);
+//   - the 16 MFMAs of O^T += V(j)^T P(j)^T with the transposed V reads two
+//     MFMAs ahead.
+// sched_barrier fences keep this order: the compiler's own schedule puts the
+// MFMAs and the softmax in separate runs.  K/V tiles of 64 keys go HBM -> LDS
+// by LDS-direct buffer loads into two stages each; the buffer range check
+// returns zeros past key M.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_bf16_common.h"
 #include "kernels.h"
@@ -27,19 +44,22 @@ namespace {
 
 using namespace bf16;
 
-constexpr int NW = 4;        // waves per workgroup
-constexpr int NT = 64 * NW;  // threads per workgroup
-constexpr int BR = 32 * NW;  // query rows per workgroup
+// Nothing is scheduled across this point.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    uint16_t *__restrict__ o, float *__restrict__ lse, float *__restrict__ part_o,
-    float *__restrict__ part_lse, int BH, int N, int M, float c, uint32_t qsign, int ntq,
-    int splits, int tiles_per_split) {
+template <int NW, int D, bool CAUSAL, bool SPLIT>
+__device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                          const uint16_t *__restrict__ v, uint16_t *__restrict__ o,
+                                          float *__restrict__ lse, float *__restrict__ part_o,
+                                          float *__restrict__ part_lse, int BH, int N, int M, float c,
+                                          uint32_t qsign, int ntq, int splits, int tiles_per_split) {
     using T = Tile<D>;
-    constexpr int LOADS = T::LOADS / NW;  // per wave per tile, for K and for V
-    static_assert(LOADS * NW == T::LOADS, "tile split");
+    constexpr int BR = 32 * NW;           // query rows per workgroup
+    constexpr int LOADS = T::LOADS / NW;  // LDS-direct loads per wave per tile, for K and for V
+    constexpr int SLOTS = 2 * (D / 16);   // score MFMAs per tile
+    constexpr int PSLOTS = 4 * (D / 32);  // P.V MFMAs per tile
+    constexpr int EVERY = SLOTS / LOADS;  // score slots per load pair
+    static_assert(LOADS * NW == T::LOADS && LOADS >= 1 && EVERY >= 1, "tile split");
     __shared__ __attribute__((aligned(1024))) char lds_k0[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_k1[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_v0[T::BYTES];
@@ -72,70 +92,161 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_bf16_kernel(
     int ld_off[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) ld_off[i] = load_src_offset<D>(wave * LOADS + i, lane);
-    auto issue = [&](int kv0, char *kdst, char *vdst, int i) {
-        const int blk = (wave * LOADS + i) * 1024;
-        const int off = (int)((uint32_t)kv0 * T::RB + (uint32_t)ld_off[i]);  // unsigned: M*d < 2^31
-        lds_direct_load16(krs, lds_addr(kdst + blk), off);
-        lds_direct_load16(vrs, lds_addr(vdst + blk), off);
+    // This wave's share i of tile `tile` of K (or V) into an LDS stage.
+    // Unsigned offsets: M * d < 2^31, so M * 2d < 2^32.
+    auto load = [&](const u32x4 &rs, int tile, char *dst, int i) {
+        const int off = (int)((uint32_t)(kb + tile * BC) * T::RB + (uint32_t)ld_off[i]);
+        lds_direct_load16(rs, lds_addr(dst + (wave * LOADS + i) * 1024), off);
     };
 
-    // The tile at kv0 from stages (ks, vs); its score MFMAs carry the loads
-    // of the next tile (at nkv0, if has_next) into the other stages.
-    auto compute_tile = [&](int kv0, const char *ks, const char *vs, bool has_next, int nkv0, char *nks,
-                            char *nvs) {
-        f32x16 s[2] = {f32x16{}, f32x16{}};
-        constexpr int EVERY = (D / 16) / LOADS;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            wt.score_step(ks, kk, s);
-            if (has_next && kk % EVERY == 0) issue(nkv0, nks, nvs, kk / EVERY);
+    // On entry s_cur = S(j); after the barrier K(j+1) is in ks_next and V(j)
+    // in vs_cur.  FULL: tile j+1 exists (its scores go to s_nxt, and K(j+2),
+    // V(j+1) are loaded into the stages every wave has finished with).  Load
+    // tile indices past the last are clamped to it: a harmless reload into a
+    // free stage that keeps the block free of branches.
+    auto iteration = [&](auto full, int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const char *ks_next,
+                         char *ks_free, const char *vs_cur, char *vs_free) {
+        constexpr bool FULL = decltype(full)::value;
+        wait_loads_and_barrier<0>();
+        wt.mask(kb + j * BC, ke, s_cur);
+        const float m = wt.m_run;
+        uint32_t popw[BC / 16][4];
+        float lsum0 = 0.f, lsum1 = 0.f;
+        bf16x8 kop[3];
+        if constexpr (FULL) {
+            s_nxt[0] = f32x16{};
+            s_nxt[1] = f32x16{};
+            kop[0] = wt.kread(ks_next, 0);
+            kop[1] = wt.kread(ks_next, 1);
         }
-        wt.mask(kv0, ke, s);
+        fence();
+#pragma unroll
+        for (int slot = 0; slot < SLOTS; ++slot) {
+            if constexpr (FULL) {
+                s_nxt[slot & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[slot % 3], wt.qop[slot >> 1],
+                                                                          s_nxt[slot & 1], 0, 0, 0);
+                if (slot + 2 < SLOTS) kop[(slot + 2) % 3] = wt.kread(ks_next, slot + 2);
+            }
+            // 32 scores over SLOTS slots: two per slot at d = 128, four at d = 64.
+#pragma unroll
+            for (int u = 0; u < 32 / SLOTS; u += 2) {
+                const int e = slot * (32 / SLOTS) + u;
+                wt.prob_pair(s_cur, e, m, popw, (e & 2) ? lsum1 : lsum0);
+            }
+            if constexpr (FULL) {
+                if (slot % EVERY == EVERY - 1) {
+                    load(krs, min(j + 2, ntiles - 1), ks_free, slot / EVERY);
+                    load(vrs, j + 1, vs_free, slot / EVERY);
+                }
+            }
+            fence();
+        }
         bf16x8 pop[BC / 16];
-        wt.softmax(s, pop);
-        wt.pv(vs, pop);
+#pragma unroll
+        for (int g = 0; g < BC / 16; ++g)
+            pop[g] = __builtin_bit_cast(bf16x8, (u32x4{popw[g][0], popw[g][1], popw[g][2], popw[g][3]}));
+        float lsum = lsum0 + lsum1;
+        // Some row's tile sum above the limit, or not finite: the exact path.
+        float alpha = 1.f;
+        if (__builtin_amdgcn_ballot_w64(!(lsum <= SHIFT_SUM_LIMIT)) != 0) alpha = wt.exact_shift(s_cur, pop, lsum);
+        wt.l_run = alpha * wt.l_run + lsum;
+
+        bf16x8 vop[3];
+        vop[0] = wt.vread(vs_cur, 0);
+        vop[1] = wt.vread(vs_cur, 1);
+        fence();
+#pragma unroll
+        for (int slot = 0; slot < PSLOTS; ++slot) {
+            const int t4 = slot / (D / 32), db = slot % (D / 32);
+            wt.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[slot % 3], pop[t4], wt.oacc[db], 0, 0, 0);
+            if (slot + 2 < PSLOTS) vop[(slot + 2) % 3] = wt.vread(vs_cur, slot + 2);
+            fence();
+        }
     };
+    using Full = std::integral_constant<bool, true>;
+    using Last = std::integral_constant<bool, false>;
 
     if (ntiles > 0) {
+        // Prologue: K(0), V(0) land; S(0) is computed while K(1) loads.
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) issue(kb, lds_k0, lds_v0, i);
-    }
-    for (int t = 0; t < ntiles; t += 2) {
-        const int kv0 = kb + t * BC;
+        for (int i = 0; i < LOADS; ++i) {
+            load(krs, 0, lds_k0, i);
+            load(vrs, 0, lds_v0, i);
+        }
         wait_loads_and_barrier<0>();
-        compute_tile(kv0, lds_k0, lds_v0, t + 1 < ntiles, kv0 + BC, lds_k1, lds_v1);
-        if (t + 1 >= ntiles) break;
-        wait_loads_and_barrier<0>();
-        compute_tile(kv0 + BC, lds_k1, lds_v1, t + 2 < ntiles, kv0 + 2 * BC, lds_k0, lds_v0);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) load(krs, min(1, ntiles - 1), lds_k1, i);
+        f32x16 sa[2] = {f32x16{}, f32x16{}}, sb[2];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) wt.score_step(lds_k0, kk, sa);
+        // Stages alternate with the parity of j: even j reads K(j+1) from k1
+        // and V(j) from v0, and refills k0 and v1.
+        int j = 0;
+        for (; j + 2 < ntiles; j += 2) {
+            iteration(Full{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+            iteration(Full{}, j + 1, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+        }
+        if (j + 2 == ntiles) {
+            iteration(Full{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+            iteration(Last{}, j + 1, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+        } else {
+            iteration(Last{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+        }
+        // The last iteration issues no loads and starts with a full wait, so
+        // no LDS-direct load is in flight past this point.
     }
 
     wt.template store<SPLIT>(N, o + (size_t)bh * N * D, lse + (size_t)bh * N,
                              part_o + ((size_t)sp * BH + bh) * N * D, part_lse + ((size_t)sp * BH + bh) * N);
 }
 
+#define ATTN_KERNEL_ARGS                                                                                       \
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,           \
+        uint16_t *__restrict__ o, float *__restrict__ lse, float *__restrict__ part_o,                        \
+        float *__restrict__ part_lse, int BH, int N, int M, float c, uint32_t qsign, int ntq, int splits,     \
+        int tiles_per_split
+#define ATTN_KERNEL_PASS q, k, v, o, lse, part_o, part_lse, BH, N, M, c, qsign, ntq, splits, tiles_per_split
+
 template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(ATTN_KERNEL_ARGS) {
+    attn_body<4, D, CAUSAL, SPLIT>(ATTN_KERNEL_PASS);
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_w8_kernel(ATTN_KERNEL_ARGS) {
+    attn_body<8, D, CAUSAL, SPLIT>(ATTN_KERNEL_PASS);
+}
+
+template <int NW, int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
-    const int ntq = (p.N + BR - 1) / BR;
+    const int rows = 32 * NW;
+    const int ntq = (p.N + rows - 1) / rows;
     const int64_t blocks = (int64_t)p.BH * ntq * p.splits;
     const uint32_t qsign = p.negate_q ? 0x80008000u : 0u;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3((unsigned)blocks), dim3(NT), 0, stream,
+    auto kernel = NW == 8 ? attn_fwd_bf16_w8_kernel<D, CAUSAL, SPLIT> : attn_fwd_bf16_kernel<D, CAUSAL, SPLIT>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * NW), 0, stream,
                        static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                        static_cast<const uint16_t *>(p.v), static_cast<uint16_t *>(p.o), p.lse, p.part_o,
                        p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split);
     return hipGetLastError();
 }
 
-template <int D>
+template <int NW, int D>
 hipError_t launch_d(const AttnProblem &p, hipStream_t stream) {
     const bool split = p.splits > 1;
-    if (p.causal) return split ? launch_t<D, true, true>(p, stream) : launch_t<D, true, false>(p, stream);
-    return split ? launch_t<D, false, true>(p, stream) : launch_t<D, false, false>(p, stream);
+    if (p.causal) return split ? launch_t<NW, D, true, true>(p, stream) : launch_t<NW, D, true, false>(p, stream);
+    return split ? launch_t<NW, D, false, true>(p, stream) : launch_t<NW, D, false, false>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream) {
-    return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
+    return p.d == 64 ? launch_d<4, 64>(p, stream) : launch_d<4, 128>(p, stream);
+}
+
+hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream) {
+    // Single pass only (the front end never asks this kernel for partials).
+    return p.d == 64 ? launch_d<8, 64>(p, stream) : launch_d<8, 128>(p, stream);
 }
 
 }  // namespace osa

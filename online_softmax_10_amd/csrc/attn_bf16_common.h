@@ -1,14 +1,15 @@
 // Shared device code of the bf16 attention kernels for gfx950: operand
-// layouts, LDS swizzle, LDS-direct loads and the per-wave tile math of the
-// online-softmax recurrence (scores, running max / sum with lazy rescale,
-// probabilities, P.V, epilogue).
+// layouts, LDS swizzle, LDS-direct loads and the per-wave pieces of the
+// online-softmax recurrence (scores, masking, probabilities against a lazily
+// moved shift, the exact fallback, the epilogue).
 //
-// Recurrence: per query row a running max m and running exponential sum l;
+// Recurrence: per query row a running shift m and running exponential sum l;
 // each new key block rescales l and the unnormalised accumulator o~ by
-// e^{m_old - m_new} and adds the block's terms; finally o = o~ / l and
-// LSE = m + log l.  Sources: "从原始Softmax到在线Softmax" page, online softmax
-// derivation (m, l, o~ recurrences) and LSE definition; "Online Softmax and
-// Flash Attention" page, eq. (8) and the fused loop of eq. (20)-(22).
+// e^{m_old - m_new} when the shift moves and adds the block's terms; finally
+// o = o~ / l and LSE = m + log l.  Sources: "从原始Softmax到在线Softmax" page,
+// online softmax derivation (m, l, o~ recurrences) and LSE definition;
+// "Online Softmax and Flash Attention" page, eq. (8) and the fused loop of
+// eq. (20)-(22).
 //
 // One wave owns 32 query rows.  Scores are computed transposed,
 // S^T = K Q^T on v_mfma_f32_32x32x16_bf16, so each lane owns one query and 16
@@ -22,8 +23,13 @@
 // scalars.  Scores stay in base-2 units: c = |scale| * log2(e) (at least the
 // smallest normal float, so masked scores of -inf give exactly 0) is folded
 // into one FMA before v_exp_f32; a negative scale flips q's sign bit on load.
-// The shift (running max) only moves when a tile's max exceeds it by a
-// slack, so most tiles skip the rescale of l and o~.
+//
+// Lazy shift: the probabilities of a tile are first formed against the
+// current shift, with no row max.  Only when some row's tile sum exceeds 2^16
+// (or is not finite -- the first tile, where the shift is still -inf) does the
+// wave take the exact path: row max, new shift, rescale of l and o~, and the
+// probabilities again.  Any shift gives the same softmax as long as numerator
+// and denominator share it and nothing overflows.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,6 +46,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -48,6 +55,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int BC = kBf16KeyTile;  // keys per tile
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994531f;
+constexpr float SHIFT_SUM_LIMIT = 65536.f;  // 2^16: largest tile sum kept against a stale shift
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data
 
 template <int D>
@@ -228,49 +236,52 @@ struct WaveTile {
         return lsum[0] + lsum[1];
     }
 
-    // One online-softmax step on the (masked) scores of a tile: the tile's row
-    // max, a new shift only when that max exceeds the current one by more
-    // than RESCALE_SLACK (base-2 units), then the rescale of l and o~ by
-    // 2^(m_old - m_new) (skipped by the whole wave when no row moved) and the
-    // tile's probabilities.  Any shift gives the same softmax as long as
-    // numerator and denominator share it and nothing overflows; with the
-    // slack, probabilities stay below 2^RESCALE_SLACK.
-    __device__ __forceinline__ void softmax(f32x16 (&s)[2], bf16x8 (&pop)[BC / 16]) {
-        constexpr float RESCALE_SLACK = 8.f;
+    // K operand of score MFMA `slot` (32-key block slot&1, feature step slot>>1).
+    __device__ __forceinline__ bf16x8 kread(const char *ks, int slot) const {
+        return *reinterpret_cast<const bf16x8 *>(ks + (slot & 1) * 32 * T::RB + k_off[slot >> 1]);
+    }
+
+    // V^T operand of P.V MFMA `slot` (key group slot / (D/32), d block
+    // slot % (D/32)): two transposing reads.
+    __device__ __forceinline__ bf16x8 vread(const char *vs, int slot) const {
+        const int t4 = slot / (D / 32), db = slot % (D / 32);
+        const char *vt = vs + t4 * 16 * T::RB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_off[0][db]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_off[1][db]));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+
+    // Probabilities of scores e, e+1 (e even; register r of block cb is score
+    // 16*cb + r) against shift m, packed to bf16 into word e/2 of popw, their
+    // sum (of the rounded values) added to acc.
+    __device__ __forceinline__ void prob_pair(const f32x16 (&s)[2], int e, float m, uint32_t (&popw)[BC / 16][4],
+                                              float &acc) const {
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        const float p0 = exp2_fast(__builtin_fmaf(s[e >> 4][e & 15], c, -m));
+        const float p1 = exp2_fast(__builtin_fmaf(s[(e + 1) >> 4][(e + 1) & 15], c, -m));
+        const bf16x2 pp = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+        popw[e >> 3][(e & 7) >> 1] = __builtin_bit_cast(uint32_t, pp);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+    }
+
+    // Exact path of one tile: row max, new shift, rescale of o~ (l is rescaled
+    // by the caller with the returned factor) and the probabilities again.
+    // Returns the factor 2^(m_old - m_new); lsum receives the new tile sum.
+    __device__ __forceinline__ float exact_shift(const f32x16 (&s)[2], bf16x8 (&pop)[BC / 16], float &lsum) {
         float mx = NEG_INF;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
         mx = xhalf_max(mx);
-        const float m_tile = mx * c;  // -inf stays -inf (c > 0)
-        const bool move = m_tile > m_run + RESCALE_SLACK;
-        const float m_new = move ? m_tile : m_run;
+        const float m_new = fmaxf(m_run, mx * c);            // -inf stays -inf (c > 0)
         const float m_use = m_new == NEG_INF ? 0.f : m_new;  // fully masked so far: p = 0
-        const float alpha = move ? exp2_fast(m_run - m_use) : 1.f;  // 0 when m_run = -inf
-        const bool any_move = __builtin_amdgcn_ballot_w64(move) != 0;
+        const float alpha = exp2_fast(m_run - m_use);         // 0 when m_run = -inf
         m_run = m_new;
-        const float lsum = probs(s, m_use, pop);
-        l_run = alpha * l_run + lsum;
-        if (any_move) {
+        lsum = probs(s, m_use, pop);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        }
-    }
-
-    // O^T += V^T P^T; each V^T operand is two transposing reads.
-    __device__ __forceinline__ void pv(const char *vs, const bf16x8 (&pop)[BC / 16]) {
-#pragma unroll
-        for (int t4 = 0; t4 < BC / 16; ++t4)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const char *vt = vs + t4 * 16 * T::RB;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_off[0][db]));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + v_off[1][db]));
-                const s16x8 w8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w8), pop[t4],
-                                                                   oacc[db], 0, 0, 0);
-            }
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        return alpha;
     }
 
     // Final o = o~ / l and LSE; bf16 output or fp32 split partial.

@@ -33,8 +33,8 @@ constexpr int kDecodeMaxQueries = 4;
 // Four-wave bf16 kernel: 128 query rows per workgroup (any size; split partials).
 hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream);
 // Eight-wave bf16 kernel: 256 query rows per workgroup, single pass only.
-hipError_t launch_attn_bf16_pp(const AttnProblem &p, hipStream_t stream);
-constexpr int kBf16PingPongRows = 256;
+hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream);
+constexpr int kBf16WideRows = 256;
 hipError_t launch_attn_f32(const AttnProblem &p, hipStream_t stream);
 // Few queries per head (N <= kDecodeMaxQueries), bf16 or fp32 inputs, always
 // writes partials (p.splits >= 1).

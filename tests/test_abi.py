@@ -133,8 +133,8 @@ def test_binding_raises_without_gpu_tensors():
 def test_plan_kernel_choice():
     # Host-only query of the decomposition: the five workload shapes and the
     # regimes between them.
-    assert osa.plan(2, 16, 4096, 4096, 128) == ("attn_fwd_bf16_pp_kernel", 1)
-    assert osa.plan(1, 8, 16384, 16384, 128) == ("attn_fwd_bf16_pp_kernel", 1)
+    assert osa.plan(2, 16, 4096, 4096, 128) == ("attn_fwd_bf16_w8_kernel", 1)
+    assert osa.plan(1, 8, 16384, 16384, 128) == ("attn_fwd_bf16_w8_kernel", 1)
     assert osa.plan(4, 8, 1024, 1024, 64) == ("attn_fwd_bf16_kernel", 1)
     name, s = osa.plan(32, 32, 1, 8192, 128)
     assert name == "attn_decode_kernel" and 1 <= s <= osa.ATTN_MAX_SPLITS
