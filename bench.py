@@ -111,6 +111,66 @@ def cpu_baseline(w: si.Workload, q, k, v, o_gpu, lse_gpu, target_s: float):
     }
 
 
+def bench_softmax(args, torch, osa) -> int:
+    """online_softmax at bandwidth scale: one read and one write of the matrix per step."""
+    import oracle
+
+    rows, n = (int(t) for t in args.softmax.lower().split("x"))
+    x_host = si.make_rows(rows, n, seed=args.seed, spread=4.0)
+    x = torch.from_numpy(x_host).cuda()
+    y = torch.empty_like(x)
+    for _ in range(args.warmup):
+        osa.online_softmax(x, out=y)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        osa.online_softmax(x, out=y)
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    nbytes = 2.0 * rows * n * 4  # x read once, y written once
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    # Oracle on evenly spaced rows (bounded), also the parity spot check.
+    sample = np.linspace(0, rows - 1, min(rows, max(2048, (1 << 26) // n))).astype(np.int64)
+    tc = time.perf_counter()
+    ref = oracle.softmax(x_host[sample].astype(np.float64))
+    dt = time.perf_counter() - tc
+    err_max = float(np.max(np.abs(y.cpu().numpy()[sample].astype(np.float64) - ref)))
+    line = {
+        "metric": "online_softmax GB/s at 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"online_softmax rows={rows} n={n} float32, N(0, 4^2) logits, seed {args.seed}",
+                   "rows": rows, "n": n},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel": "online_softmax",
+                     "launch_us": round(launch_ms * 1e3, 2), "algorithmic_bytes": nbytes},
+        "cpu_baseline": {"value": round(2.0 * len(sample) * n * 4 / dt / 1e9, 3), "unit": "GB/s",
+                         "cores": oracle.num_threads(),
+                         "kind": "oracle", "sample": f"{len(sample)} of {rows} rows, evenly spaced ({dt:.2f} s)"},
+        "max_abs_err_vs_oracle": err_max,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +180,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--softmax", default="", metavar="ROWSxN",
+                    help="instead of attention, time the row-wise online_softmax on a ROWS x N float32 matrix "
+                         "(e.g. 32768x1024: the rows and key count of the 4x8x1024 workload)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -146,6 +209,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": args.steps}), flush=True)
         return 0
+    if args.softmax:
+        return bench_softmax(args, torch, osa)
     w = si.WORKLOADS[args.workload]
     err(f"[bench] workload {w}")
     q, k, v = si.make_qkv(w, args.seed)

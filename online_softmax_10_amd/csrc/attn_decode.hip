@@ -6,7 +6,8 @@
 // bound by streaming K and V from HBM, not by arithmetic: it uses plain fp32
 // VALU FMAs instead of MFMA (whose 32-wide query dimension would be >= 87%
 // padding here) and spends its registers on keeping many 16-byte loads in
-// flight.
+// flight.  K and V are read exactly once, so the loads are non-temporal (no
+// cache allocation for data nobody reads again).
 //
 // Recurrence (per query row, per group of keys): running max m, running sum
 // l, accumulator o~ rescaled by e^{m_old - m_new}: "从原始Softmax到在线Softmax"
@@ -28,7 +29,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NW = 4;
 constexpr int NT = 64 * NW;
-constexpr int U = 4;  // key groups per wave per iteration (loads in flight)
+constexpr int U = 8;  // key groups per wave per iteration (loads in flight)
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994531f;
 
@@ -124,8 +125,8 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const void *__restri
             key[u] = base + wave * KPW * U + u * KPW + g;
             // past the range: reload the last valid key (masked below, weight exactly 0)
             const int kc = min(key[u], ke - 1);
-            kr[u] = *reinterpret_cast<const u32x4 *>(kh + ((size_t)kc * D + e0) * ESZ);
-            vr[u] = *reinterpret_cast<const u32x4 *>(vh + ((size_t)kc * D + e0) * ESZ);
+            kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kh + ((size_t)kc * D + e0) * ESZ));
+            vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vh + ((size_t)kc * D + e0) * ESZ));
         }
         float kf[U][EPL], vf[U][EPL];
 #pragma unroll

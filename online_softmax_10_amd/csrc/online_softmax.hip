@@ -5,7 +5,9 @@
 // + e^{x_i - m_i}), a chunk of four elements at a time; the 64 lane states are
 // merged with the same rule (max of the two maxima, each sum rescaled to it).
 // Pass 2 writes y = e^{x - m} / s.  Two reads and one write per element,
-// against three reads and one write for the three-pass safe softmax.
+// against three reads and one write for the three-pass safe softmax; rows of
+// up to 4096 elements (a multiple of 4) stay in registers between the passes,
+// so they are read once.
 // Sources: "Online Softmax and Flash Attention" page, section "Online softmax",
 // eq. (3)-(7) and the pass counts in its introduction; "Softmax与Flash-Attention"
 // page, online-softmax derivation.
@@ -95,6 +97,50 @@ __device__ __forceinline__ void softmax_row(const float *xr, float *yr, int64_t 
     }
 }
 
+// Rows of n <= 256*R elements (n % 4 == 0) held in registers: each lane keeps
+// R float4 chunks (chunk i + 64 r of the row), so the row is read once.
+template <int R>
+__device__ __forceinline__ void softmax_row_regs(const float *xr, float *yr, int64_t n, int lane) {
+    const int64_t nv = n >> 2;
+    f32x4 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t i = lane + 64 * r;
+        v[r] = i < nv ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(xr) + i)
+                      : f32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    }
+    MS st{NEG_INF, 0.f};
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float t[4] = {v[r][0], v[r][1], v[r][2], v[r][3]};
+        absorb<4>(st, t);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        MS o{__shfl_xor(st.sh, off, 64), __shfl_xor(st.s, off, 64)};
+        st = merge(st, o);
+    }
+    const float sh = st.sh;
+    const float inv = 1.f / st.s;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t i = lane + 64 * r;
+        if (i < nv) {
+            f32x4 y;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[r][j], LOG2E, -sh)) * inv;
+            __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(yr) + i);
+        }
+    }
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void online_softmax_regs_kernel(const float *x, float *y, int64_t rows, int64_t n) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4)
+        softmax_row_regs<R>(x + row * n, y + row * n, n, lane);
+}
+
 // Grid-stride over rows, one wave per row.
 template <bool VEC>
 __global__ __launch_bounds__(256) void online_softmax_kernel(const float *x, float *y,
@@ -109,7 +155,19 @@ __global__ __launch_bounds__(256) void online_softmax_kernel(const float *x, flo
 hipError_t launch_online_softmax(const float *x, float *y, int64_t rows, int64_t n, hipStream_t stream) {
     const int64_t want = (rows + 3) / 4;
     const dim3 grid((unsigned)(want < 65536 ? want : 65536));
-    if ((n & 3) == 0)
+    if ((n & 3) == 0 && n <= 4096) {
+        // Smallest power-of-two chunk count per lane that holds the row.
+        if (n <= 256)
+            hipLaunchKernelGGL((online_softmax_regs_kernel<1>), grid, dim3(256), 0, stream, x, y, rows, n);
+        else if (n <= 512)
+            hipLaunchKernelGGL((online_softmax_regs_kernel<2>), grid, dim3(256), 0, stream, x, y, rows, n);
+        else if (n <= 1024)
+            hipLaunchKernelGGL((online_softmax_regs_kernel<4>), grid, dim3(256), 0, stream, x, y, rows, n);
+        else if (n <= 2048)
+            hipLaunchKernelGGL((online_softmax_regs_kernel<8>), grid, dim3(256), 0, stream, x, y, rows, n);
+        else
+            hipLaunchKernelGGL((online_softmax_regs_kernel<16>), grid, dim3(256), 0, stream, x, y, rows, n);
+    } else if ((n & 3) == 0)
         hipLaunchKernelGGL((online_softmax_kernel<true>), grid, dim3(256), 0, stream, x, y, rows, n);
     else
         hipLaunchKernelGGL((online_softmax_kernel<false>), grid, dim3(256), 0, stream, x, y, rows, n);
