@@ -5,9 +5,10 @@
 // + e^{x_i - m_i}), a chunk of four elements at a time; the 64 lane states are
 // merged with the same rule (max of the two maxima, each sum rescaled to it).
 // Pass 2 writes y = e^{x - m} / s.  Two reads and one write per element,
-// against three reads and one write for the three-pass safe softmax; rows of
-// up to 4096 elements (a multiple of 4) stay in registers between the passes,
-// so they are read once.
+// against three reads and one write for the three-pass safe softmax.  Rows
+// whose length is a multiple of 4 and at most 65536 stay in registers between
+// the passes, so they are read once: up to 4096 elements in one wave, longer
+// rows in a 1024-thread workgroup that merges its 16 wave states through LDS.
 // Sources: "Online Softmax and Flash Attention" page, section "Online softmax",
 // eq. (3)-(7) and the pass counts in its introduction; "Softmax与Flash-Attention"
 // page, online-softmax derivation.
@@ -141,6 +142,56 @@ __global__ __launch_bounds__(256) void online_softmax_regs_kernel(const float *x
         softmax_row_regs<R>(x + row * n, y + row * n, n, lane);
 }
 
+// Rows of 4096 < n <= 1024*4*R elements (n % 4 == 0): one 1024-thread
+// workgroup per row, R float4 chunks per thread (chunk t + 1024 r), wave
+// states merged through LDS.
+template <int R>
+__global__ __launch_bounds__(1024) void online_softmax_wide_kernel(const float *x, float *y, int64_t rows,
+                                                                   int64_t n) {
+    __shared__ MS part[16];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t nv = n >> 2;
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const f32x4 *xr = reinterpret_cast<const f32x4 *>(x + row * n);
+        f32x4 *yr = reinterpret_cast<f32x4 *>(y + row * n);
+        f32x4 v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t i = t + 1024 * r;
+            v[r] = i < nv ? __builtin_nontemporal_load(xr + i) : f32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+        }
+        MS st{NEG_INF, 0.f};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float tt[4] = {v[r][0], v[r][1], v[r][2], v[r][3]};
+            absorb<4>(st, tt);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            MS o{__shfl_xor(st.sh, off, 64), __shfl_xor(st.s, off, 64)};
+            st = merge(st, o);
+        }
+        if (lane == 0) part[wave] = st;
+        __syncthreads();
+        MS all = part[0];
+#pragma unroll
+        for (int w = 1; w < 16; ++w) all = merge(all, part[w]);
+        __syncthreads();  // part[] is rewritten by the next row
+        const float sh = all.sh;
+        const float inv = 1.f / all.s;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t i = t + 1024 * r;
+            if (i < nv) {
+                f32x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[r][j], LOG2E, -sh)) * inv;
+                __builtin_nontemporal_store(o, yr + i);
+            }
+        }
+    }
+}
+
 // Grid-stride over rows, one wave per row.
 template <bool VEC>
 __global__ __launch_bounds__(256) void online_softmax_kernel(const float *x, float *y,
@@ -167,6 +218,16 @@ hipError_t launch_online_softmax(const float *x, float *y, int64_t rows, int64_t
             hipLaunchKernelGGL((online_softmax_regs_kernel<8>), grid, dim3(256), 0, stream, x, y, rows, n);
         else
             hipLaunchKernelGGL((online_softmax_regs_kernel<16>), grid, dim3(256), 0, stream, x, y, rows, n);
+    } else if ((n & 3) == 0 && n <= 65536) {
+        const dim3 wgrid((unsigned)(rows < 65536 ? rows : 65536));
+        if (n <= 8192)
+            hipLaunchKernelGGL((online_softmax_wide_kernel<2>), wgrid, dim3(1024), 0, stream, x, y, rows, n);
+        else if (n <= 16384)
+            hipLaunchKernelGGL((online_softmax_wide_kernel<4>), wgrid, dim3(1024), 0, stream, x, y, rows, n);
+        else if (n <= 32768)
+            hipLaunchKernelGGL((online_softmax_wide_kernel<8>), wgrid, dim3(1024), 0, stream, x, y, rows, n);
+        else
+            hipLaunchKernelGGL((online_softmax_wide_kernel<16>), wgrid, dim3(1024), 0, stream, x, y, rows, n);
     } else if ((n & 3) == 0)
         hipLaunchKernelGGL((online_softmax_kernel<true>), grid, dim3(256), 0, stream, x, y, rows, n);
     else

@@ -43,7 +43,8 @@ def test_c1_softmax_row_worked_example():
     assert abs(-math.log(y[0, 0]) - g2["loss"]) <= g2["tol_printed"]
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 63, 64, 65, 256, 260, 512, 1000, 2048, 3000, 4096, 4097, 4100, 65536])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 63, 64, 65, 256, 260, 512, 1000, 2048, 3000, 4096, 4097, 4100,
+                               8192, 12000, 16388, 32768, 50000, 65536, 65540, 70000])
 def test_rows_match_oracle(n):
     rows = 37 if n <= 4096 else 5
     x = si.make_rows(rows, n, seed=n, spread=4.0)
