@@ -7,8 +7,8 @@ library (``online_softmax_10_amd``) and never imports it.
 Two parts:
 
 * ``liboracle.so`` (``oracle.c``): the plain definitions in float64 -- three-pass
-  safe softmax, log-sum-exp, the one-pass normaliser recurrence, and exact
-  attention softmax(mask(Q K^T scale)) V with its row LSE.
+  safe softmax, log-sum-exp, softmax cross-entropy, the one-pass normaliser
+  recurrence, and exact attention softmax(mask(Q K^T scale)) V with its row LSE.
 * ``recurrences`` (pure Python/numpy, small inputs only): the pages' other
   formulations -- the two-loop attention, the per-step normalised recurrence
   and the blocked (m, l, o~) recurrence with its merge form -- used only to
@@ -48,13 +48,14 @@ _i64 = ctypes.c_int64
 def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_softmax_f64.argtypes = [_f64p, _f64p, _i64, _i64]
     lib.oracle_logsumexp_f64.argtypes = [_f64p, _f64p, _i64, _i64]
+    lib.oracle_xent_f64.argtypes = [_f64p, _i64p, _f64p, _f64p, _i64, _i64]
     lib.oracle_online_normalizer_f64.argtypes = [_f64p, _f64p, _f64p, _i64, _i64]
     lib.oracle_attn_rows_f64.argtypes = [_f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64,
                                          ctypes.c_double, ctypes.c_int, _i64p, _i64, _f64p, _f64p]
     lib.oracle_attn_f64.argtypes = [_f64p, _f64p, _f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64,
                                     ctypes.c_double, ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
-    for name in ("oracle_softmax_f64", "oracle_logsumexp_f64", "oracle_online_normalizer_f64",
+    for name in ("oracle_softmax_f64", "oracle_logsumexp_f64", "oracle_xent_f64", "oracle_online_normalizer_f64",
                  "oracle_attn_rows_f64", "oracle_attn_f64"):
         getattr(lib, name).restype = None
     return lib
@@ -99,6 +100,26 @@ def logsumexp(x, lib=None) -> np.ndarray:
     out = np.empty(x.shape[:-1], dtype=np.float64)
     (lib or load()).oracle_logsumexp_f64(_p(x), _p(out), x.size // n, n)
     return out
+
+
+def cross_entropy(x, labels, lib=None):
+    """Per-row softmax cross-entropy, row LSE and their mean over rows.
+
+    x [rows, n], labels [rows] integer class indices.  Returns (loss [rows],
+    lse [rows], mean): loss_i = -log softmax(x_i)[labels_i] (NaN for a label
+    outside [0, n)), mean = the page's batch mean of the losses (math.fsum).
+    """
+    import math
+
+    x = _c64(x)
+    n = x.shape[-1]
+    rows = x.size // n
+    lab = np.ascontiguousarray(np.asarray(labels, dtype=np.int64).reshape(rows))
+    loss = np.empty(rows, dtype=np.float64)
+    lse = np.empty(rows, dtype=np.float64)
+    (lib or load()).oracle_xent_f64(_p(x), lab.ctypes.data_as(_i64p), _p(loss), _p(lse), rows, n)
+    mean = math.fsum(loss.tolist()) / rows if rows else float("nan")
+    return loss, lse, mean
 
 
 def online_normalizer(x, lib=None):

@@ -70,6 +70,39 @@ void oracle_logsumexp_f64(const double *x, double *lse, int64_t rows, int64_t n)
 }
 
 /*
+ * Softmax cross-entropy of each row against its class label, and the row LSE.
+ * Source: "从原始Softmax到在线Softmax" page, section "softmax实际代码实现" (the
+ * cross-entropy loss: row max, shifted exponentials and their sum, log
+ * probabilities z - max - log(sum), the label's entry, negated) and the
+ * log-softmax / LSE definitions of "softmax形式推导".
+ * x: row-major [rows, n], n >= 1; labels: [rows].  A label outside [0, n) has
+ * no log probability: its loss is NaN.
+ */
+void oracle_xent_f64(const double *x, const int64_t *labels, double *loss, double *lse, int64_t rows, int64_t n)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        const double *xr = x + r * n;
+        double m = xr[0];
+        for (int64_t j = 1; j < n; ++j)
+            if (xr[j] > m) m = xr[j];
+        double s = 0.0;
+        for (int64_t j = 0; j < n; ++j)
+            s += exp(xr[j] - m);
+        const double log_sum = log(s);
+        lse[r] = m + log_sum;
+        const int64_t c = labels[r];
+        if (c < 0 || c >= n) {
+            loss[r] = NAN;
+        } else {
+            const double log_prob = xr[c] - m - log_sum;
+            loss[r] = -log_prob;
+        }
+    }
+}
+
+/*
  * The one-pass normaliser recurrence, element by element:
  *   m_i = max(m_{i-1}, x_i),   s_i = s_{i-1} * e^{m_{i-1} - m_i} + e^{x_i - m_i},
  * started from m_1 = x_1, s_1 = 1.

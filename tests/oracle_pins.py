@@ -296,9 +296,53 @@ def pin_formulations_agree(lib):
             close(g3 + math.log(s3), lse[0, 0, i], 1e-13, f"stepwise g_M + log s_M row {i}")
 
 
+def pin_cross_entropy(lib):
+    # The worked example: logits [2, 1, 0.1], class 0.
+    g = golden("w2_cross_entropy.json")
+    loss, lse, mean = oracle.cross_entropy(np.array([g["logits"]]), [g["label"]], lib)
+    close(loss[0], g["loss"], g["tol_printed"], "W2 cross-entropy vs printed")
+    close(mean, g["loss"], g["tol_printed"], "W2 batch mean of one row")
+    # torch's float64 cross-entropy on small random batches (per row and mean).
+    import torch
+    import torch.nn.functional as F
+
+    for seed, (rows, n, spread) in enumerate(((7, 5, 3.0), (4, 33, 10.0), (3, 1, 1.0))):
+        x = _rand((rows, n), 100 + seed, spread)
+        lab = np.random.default_rng(200 + seed).integers(0, n, size=rows)
+        loss, lse, mean = oracle.cross_entropy(x, lab, lib)
+        xt, lt = torch.from_numpy(x), torch.from_numpy(lab)
+        close(loss, F.cross_entropy(xt, lt, reduction="none").numpy(), 1e-12, f"torch cross_entropy {rows}x{n}")
+        close(mean, float(F.cross_entropy(xt, lt, reduction="mean")), 1e-12, f"torch mean {rows}x{n}")
+        close(lse, torch.logsumexp(xt, dim=1).numpy(), 1e-12, f"torch logsumexp {rows}x{n}")
+    # Closed forms: equal logits give log n for any label; two classes give the
+    # softplus of the logit gap; a dominant label logit gives ~0 without overflow.
+    for n in (1, 2, 3, 10, 1000):
+        x = np.full((3, n), 7.25)
+        loss, _, _ = oracle.cross_entropy(x, [0, n - 1, n // 2], lib)
+        close(loss, [math.log(n)] * 3, 1e-12, f"uniform logits n={n}")
+    for a, b in ((0.0, 0.0), (2.0, -1.0), (-3.5, 4.25), (30.0, -30.0)):
+        loss, _, _ = oracle.cross_entropy(np.array([[a, b]]), [0], lib)
+        close(loss[0], math.log1p(math.exp(b - a)), 1e-12, f"two-class softplus {a},{b}")
+    loss, lse, _ = oracle.cross_entropy(np.array([[1000.0, 0.0, -5.0]]), [0], lib)
+    close(loss[0], 0.0, 1e-300 + 1e-15, "dominant label, huge logit")
+    close(lse[0], 1000.0, 1e-12, "LSE of a dominant huge logit")
+    # Shift invariance of the loss; the LSE moves with the shift.
+    x = _rand((5, 17), 7, 2.0)
+    lab = np.arange(5) * 3
+    l0, s0, _ = oracle.cross_entropy(x, lab, lib)
+    l1, s1, _ = oracle.cross_entropy(x + 750.0, lab, lib)
+    close(l1, l0, 1e-9, "loss shift invariance")
+    close(s1 - 750.0, s0, 1e-9, "LSE shift")
+    close(l0, s0 - x[np.arange(5), lab], 1e-12, "loss = LSE - z_label")
+    # A label outside [0, n) has no log probability.
+    loss, _, _ = oracle.cross_entropy(np.zeros((3, 4)), [-1, 4, 2], lib)
+    assert math.isnan(loss[0]) and math.isnan(loss[1]) and abs(loss[2] - math.log(4)) < 1e-12, loss
+
+
 ALL_PINS = [
     pin_w1_softmax,
     pin_w2_cross_entropy,
+    pin_cross_entropy,
     pin_w3_attention,
     pin_w4_online_merge,
     pin_softmax_identities,

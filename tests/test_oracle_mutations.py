@@ -36,6 +36,13 @@ MUTATIONS = [
     ("LSE of softmax rows without the max", "lse[r] = m + log(s);", "lse[r] = log(s);"),
     ("query row ignores the head", "const double *qi = q + r * d;", "const double *qi = q + i * d;"),
     ("every head uses head 0's keys", "const double *kh = k + bh * M * d;", "const double *kh = k;"),
+    ("cross-entropy sign flipped", "loss[r] = -log_prob;", "loss[r] = log_prob;"),
+    ("cross-entropy label off by one", "const double log_prob = xr[c] - m - log_sum;",
+     "const double log_prob = xr[(c + 1) % n] - m - log_sum;"),
+    ("cross-entropy without the max", "const double log_prob = xr[c] - m - log_sum;",
+     "const double log_prob = xr[c] - log_sum;"),
+    ("cross-entropy LSE without the max", "lse[r] = m + log_sum;", "lse[r] = log_sum;"),
+    ("cross-entropy invalid label scored", "loss[r] = NAN;", "loss[r] = 0.0;"),
 ]
 
 
