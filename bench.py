@@ -171,6 +171,67 @@ def bench_softmax(args, torch, osa) -> int:
     return 0
 
 
+def bench_xent(args, torch, osa) -> int:
+    """softmax_xent at bandwidth scale: the logits are read once per step."""
+    import oracle
+
+    rows, n = (int(t) for t in args.xent.lower().split("x"))
+    x_host = si.make_rows(rows, n, seed=args.seed, spread=4.0)
+    lab_host = np.random.default_rng(args.seed + 1).integers(0, n, size=rows).astype(np.int64)
+    x = torch.from_numpy(x_host).cuda()
+    lab = torch.from_numpy(lab_host).cuda()
+    loss = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    lse = torch.empty_like(loss)
+    for _ in range(args.warmup):
+        osa.softmax_xent(x, lab, out=loss, lse=lse)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        _, _, mean = osa.softmax_xent(x, lab, out=loss, lse=lse)
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    nbytes = rows * n * 4.0 + rows * (8 + 4 + 4) + 4  # logits once, labels, loss, lse, mean
+    sample = np.linspace(0, rows - 1, min(rows, max(512, (1 << 25) // n))).astype(np.int64)
+    tc = time.perf_counter()
+    ref_loss, ref_lse, _ = oracle.cross_entropy(x_host[sample].astype(np.float64), lab_host[sample])
+    dt = time.perf_counter() - tc
+    got = loss.cpu().numpy()[sample].astype(np.float64)
+    line = {
+        "metric": "softmax_xent GB/s at 1 GPU",
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"softmax_xent rows={rows} n={n} float32, N(0, 4^2) logits, uniform labels, "
+                               f"seed {args.seed}", "rows": rows, "n": n},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (launch_ms * 1e-3) / 1e9, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(nbytes / (launch_ms * 1e-3) / 1e9 / 8000.0, 4), "traffic": None,
+                     "kernel": "softmax_xent_kernel + xent_mean_kernel", "launch_us": round(launch_ms * 1e3, 2),
+                     "algorithmic_bytes": nbytes},
+        "cpu_baseline": {"value": round(len(sample) * n * 4.0 / dt / 1e9, 3), "unit": "GB/s",
+                         "cores": oracle.num_threads(), "kind": "oracle",
+                         "sample": f"{len(sample)} of {rows} rows, evenly spaced ({dt:.2f} s)"},
+        "max_abs_err_vs_oracle": {"loss": float(np.max(np.abs(got - ref_loss)))},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +244,9 @@ def main() -> int:
     ap.add_argument("--softmax", default="", metavar="ROWSxN",
                     help="instead of attention, time the row-wise online_softmax on a ROWS x N float32 matrix "
                          "(e.g. 32768x1024: the rows and key count of the 4x8x1024 workload)")
+    ap.add_argument("--xent", default="", metavar="ROWSxN",
+                    help="instead of attention, time softmax_xent (per-row cross-entropy + mean) on ROWS x N "
+                         "float32 logits (e.g. 8192x32000)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -211,6 +275,8 @@ def main() -> int:
         return 0
     if args.softmax:
         return bench_softmax(args, torch, osa)
+    if args.xent:
+        return bench_xent(args, torch, osa)
     w = si.WORKLOADS[args.workload]
     err(f"[bench] workload {w}")
     q, k, v = si.make_qkv(w, args.seed)

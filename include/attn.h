@@ -138,6 +138,39 @@ int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stre
 const char *attn_strerror(int code);
 
 /*
+ * softmax_xent -- softmax cross-entropy of each row against a class label,
+ * with the log-sum-exp taken in one pass by the online normaliser.
+ *
+ *   loss[i] = LSE_i - x[i, labels[i]],   LSE_i = log sum_j e^{x[i,j]}  (natural log)
+ *   mean    = (1/rows) sum_i loss[i]
+ *
+ * The loss of a row is the negated log probability of its label under the
+ * row's softmax, and the batch loss is their mean ("从原始Softmax到在线Softmax"
+ * page, "softmax实际代码实现" and "softmax形式推导"); the LSE is formed with
+ * the one-pass normaliser of the "Online Softmax and Flash Attention" page,
+ * section "Online softmax", eq. (3)-(7), so the logits are read once.
+ *
+ * x      [rows, n] fp32 logits, row-major, device, 16-byte aligned (read only)
+ * labels [rows] int64 class indices, device, 8-byte aligned (read only); a
+ *        label outside [0, n) makes that row's loss NaN (and so the mean)
+ * loss   [rows] fp32, device, written
+ * lse    [rows] fp32, device, written; may be NULL
+ * mean   one fp32, device, written; may be NULL.  Added in fp64 in a fixed
+ *        order (deterministic).
+ * All buffers are caller-owned; the call is asynchronous on `stream` (a
+ * hipStream_t; NULL = the null stream) and allocates nothing.
+ *
+ * Errors (before any HIP call): ATTN_ERR_SHAPE for rows < 0, n < 0, or
+ * n < 1 with rows > 0; ATTN_ERR_NULL for a NULL x, labels or loss;
+ * ATTN_ERR_ALIGN for misaligned pointers; ATTN_ERR_OVERFLOW when rows * n
+ * or n exceeds the index range.  rows == 0 is a no-op returning ATTN_OK
+ * (mean is not written).  A row of only -inf logits has LSE -inf and a NaN
+ * loss.
+ */
+int softmax_xent(const float *x, const int64_t *labels, float *loss, float *lse, float *mean, int64_t rows,
+                 int64_t n, void *stream);
+
+/*
  * attn_fwd_plan -- the work decomposition attn_fwd_splits would use, without
  * launching anything (host only; needs no GPU).
  *

@@ -7,6 +7,7 @@ missing or a call fails, an exception is raised.
 
     o, lse = fwd(q, k, v, scale=None, causal=False)      # q [B,H,N,d], k/v [B,H,M,d]
     y = online_softmax(x)                                  # x [rows, n] float32
+    loss, lse, mean = softmax_xent(x, labels)              # labels [rows] int64
 """
 
 from __future__ import annotations
@@ -15,7 +16,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_splits", "online_softmax", "plan", "lib", "LIB_PATH", "AttnError",
+__all__ = ["fwd", "fwd_splits", "online_softmax", "softmax_xent", "plan", "lib", "LIB_PATH", "AttnError",
            "ATTN_F32", "ATTN_BF16", "ATTN_MAX_SPLITS", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -26,8 +27,8 @@ ATTN_MAX_SPLITS = 256
 ERROR_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
                -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_OVERFLOW", -7: "ATTN_ERR_HIP",
                -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_SPLITS"}
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "online_softmax", "attn_fwd_plan", "attn_strerror",
-                    "attn_last_error_detail")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "online_softmax", "softmax_xent", "attn_fwd_plan",
+                    "attn_strerror", "attn_last_error_detail")
 
 _lib = None
 
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_error_detail.argtypes = []
         L.attn_last_error_detail.restype = ctypes.c_char_p
+        L.softmax_xent.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp]
+        L.softmax_xent.restype = ctypes.c_int
         L.attn_fwd_plan.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.POINTER(ctypes.c_int)]
         L.attn_fwd_plan.restype = ctypes.c_char_p
@@ -171,3 +174,38 @@ def online_softmax(x, out=None):
     if rc != 0:
         raise AttnError(rc, "online_softmax")
     return out
+
+
+def softmax_xent(x, labels, out=None, lse=None, mean=True):
+    """Per-row softmax cross-entropy against integer labels.
+
+    x: contiguous float32 GPU tensor, softmax over its last axis (rows = the
+    product of the other axes); labels: contiguous int64 GPU tensor with one
+    label per row.  Returns (loss [rows] float32, lse [rows] float32, mean: a
+    one-element float32 tensor, or None when mean=False).  A label outside
+    [0, n) gives a NaN loss for its row.
+    """
+    import torch
+
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be a contiguous float32 GPU tensor with at least one axis")
+    n = x.shape[-1]
+    rows = x.numel() // n if n > 0 else 0
+    if labels.dtype != torch.int64 or not labels.is_contiguous() or labels.device != x.device:
+        raise ValueError("labels must be a contiguous int64 tensor on x's device")
+    if labels.numel() != rows:
+        raise ValueError(f"labels has {labels.numel()} entries for {rows} rows")
+    if out is None:
+        out = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    else:
+        _check_output("out", out, (rows,), torch.float32, x.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    else:
+        _check_output("lse", lse, (rows,), torch.float32, x.device)
+    m = torch.empty((1,), dtype=torch.float32, device=x.device) if mean else None
+    rc = lib().softmax_xent(x.data_ptr(), labels.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            m.data_ptr() if m is not None else None, rows, n, _stream_handle(x.device))
+    if rc != 0:
+        raise AttnError(rc, "softmax_xent")
+    return out, lse, m

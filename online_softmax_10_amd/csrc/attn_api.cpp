@@ -214,6 +214,25 @@ int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stre
     return ATTN_OK;
 }
 
+int softmax_xent(const float *x, const int64_t *labels, float *loss, float *lse, float *mean, int64_t rows,
+                 int64_t n, void *stream) {
+    if (rows < 0 || n < 0) return ATTN_ERR_SHAPE;
+    if (rows == 0) return ATTN_OK;
+    if (n < 1) return ATTN_ERR_SHAPE;
+    if (!x || !labels || !loss) return ATTN_ERR_NULL;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(labels) & 7u) || (reinterpret_cast<uintptr_t>(loss) & 3u) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (mean && (reinterpret_cast<uintptr_t>(mean) & 3u)))
+        return ATTN_ERR_ALIGN;
+    if (n > kI32Max || rows > (int64_t(1) << 62) / n) return ATTN_ERR_OVERFLOW;
+    const hipError_t e =
+        osa::launch_softmax_xent(x, labels, loss, lse, mean, rows, n, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        set_detail("softmax cross-entropy kernel launch", e);
+        return ATTN_ERR_HIP;
+    }
+    return ATTN_OK;
+}
+
 const char *attn_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int d, int dtype, int num_splits,
                           int *splits) {
     if (splits) *splits = 0;

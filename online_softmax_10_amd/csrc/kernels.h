@@ -43,5 +43,9 @@ hipError_t launch_attn_decode(const AttnProblem &p, bool bf16, hipStream_t strea
 hipError_t launch_split_merge(const AttnProblem &p, bool bf16, hipStream_t stream);
 
 hipError_t launch_online_softmax(const float *x, float *y, int64_t rows, int64_t n, hipStream_t stream);
+// loss[i] = LSE_i - x[i, labels[i]] (NaN for a label outside [0, n)); lse and
+// mean optional (nullptr): the row LSE and the mean of the losses.
+hipError_t launch_softmax_xent(const float *x, const int64_t *labels, float *loss, float *lse, float *mean,
+                               int64_t rows, int64_t n, hipStream_t stream);
 
 }  // namespace osa

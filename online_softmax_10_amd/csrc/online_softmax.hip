@@ -13,8 +13,10 @@
 // eq. (3)-(7) and the pass counts in its introduction; "Softmax与Flash-Attention"
 // page, online-softmax derivation.
 //
-// One 64-wide wave per row, four rows per workgroup.  Exponentials are
-// v_exp_f32 on base-2 arguments: e^{x - m} = 2^{x*log2(e) - m*log2(e)}, one FMA.
+// One 64-wide wave per row (or a 1024-thread workgroup for long rows).
+// Exponentials are v_exp_f32 on base-2 arguments, e^{x - m} = 2^{(x - m)
+// log2(e)}: the difference x - m is exact for nearby values, so logits of any
+// magnitude work.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,13 +31,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LOG2E = 1.4426950408889634f;
 
-// Running state of the recurrence, kept in base-2 units: sh = m * log2(e)
-// (rounded once) is the shift and s = sum_i 2^{x_i log2(e) - sh}.  Every
-// rescale uses differences of stored shifts, so numerator and denominator
-// always share exactly the same shift.
+// Running state of the recurrence: the max m so far and s = sum_i e^{x_i - m}.
 struct MS {
-    float sh, s;
+    float m, s;
 };
+
+// e^{a - b} = 2^{(a - b) log2(e)} (0 for a = -inf, b finite).
+__device__ __forceinline__ float exp_diff(float a, float b) { return __builtin_amdgcn_exp2f((a - b) * LOG2E); }
 
 // Fold the values x[0..CNT) into the state.
 template <int CNT>
@@ -43,21 +45,21 @@ __device__ __forceinline__ void absorb(MS &st, const float *x) {
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < CNT; ++i) mx = fmaxf(mx, x[i]);
-    const float sh_new = fmaxf(st.sh, mx * LOG2E);
-    if (sh_new == NEG_INF) return;  // only -inf seen so far
+    const float m_new = fmaxf(st.m, mx);
+    if (m_new == NEG_INF) return;  // only -inf seen so far
     float add = 0.f;
 #pragma unroll
-    for (int i = 0; i < CNT; ++i) add += __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], LOG2E, -sh_new));
-    st.s = st.s * __builtin_amdgcn_exp2f(st.sh - sh_new) + add;
-    st.sh = sh_new;
+    for (int i = 0; i < CNT; ++i) add += exp_diff(x[i], m_new);
+    st.s = st.s * exp_diff(st.m, m_new) + add;
+    st.m = m_new;
 }
 
 __device__ __forceinline__ MS merge(MS a, MS b) {
-    const float sh = fmaxf(a.sh, b.sh);
-    if (sh == NEG_INF) return a;
-    const float sa = a.sh == NEG_INF ? 0.f : a.s * __builtin_amdgcn_exp2f(a.sh - sh);
-    const float sb = b.sh == NEG_INF ? 0.f : b.s * __builtin_amdgcn_exp2f(b.sh - sh);
-    return MS{sh, sa + sb};
+    const float m = fmaxf(a.m, b.m);
+    if (m == NEG_INF) return a;
+    const float sa = a.m == NEG_INF ? 0.f : a.s * exp_diff(a.m, m);
+    const float sb = b.m == NEG_INF ? 0.f : b.s * exp_diff(b.m, m);
+    return MS{m, sa + sb};
 }
 
 template <bool VEC>
@@ -79,10 +81,10 @@ __device__ __forceinline__ void softmax_row(const float *xr, float *yr, int64_t 
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-        MS o{__shfl_xor(st.sh, off, 64), __shfl_xor(st.s, off, 64)};
+        MS o{__shfl_xor(st.m, off, 64), __shfl_xor(st.s, off, 64)};
         st = merge(st, o);
     }
-    const float sh = st.sh;
+    const float m = st.m;
     const float inv = 1.f / st.s;
     if constexpr (VEC) {
         const int64_t nv = n >> 2;
@@ -90,11 +92,11 @@ __device__ __forceinline__ void softmax_row(const float *xr, float *yr, int64_t 
             const f32x4 v = reinterpret_cast<const f32x4 *>(xr)[i];
             f32x4 r;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[j], LOG2E, -sh)) * inv;
+            for (int j = 0; j < 4; ++j) r[j] = exp_diff(v[j], m) * inv;
             reinterpret_cast<f32x4 *>(yr)[i] = r;
         }
     } else {
-        for (int64_t i = lane; i < n; i += 64) yr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xr[i], LOG2E, -sh)) * inv;
+        for (int64_t i = lane; i < n; i += 64) yr[i] = exp_diff(xr[i], m) * inv;
     }
 }
 
@@ -118,10 +120,10 @@ __device__ __forceinline__ void softmax_row_regs(const float *xr, float *yr, int
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-        MS o{__shfl_xor(st.sh, off, 64), __shfl_xor(st.s, off, 64)};
+        MS o{__shfl_xor(st.m, off, 64), __shfl_xor(st.s, off, 64)};
         st = merge(st, o);
     }
-    const float sh = st.sh;
+    const float m = st.m;
     const float inv = 1.f / st.s;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -129,7 +131,7 @@ __device__ __forceinline__ void softmax_row_regs(const float *xr, float *yr, int
         if (i < nv) {
             f32x4 y;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) y[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[r][j], LOG2E, -sh)) * inv;
+            for (int j = 0; j < 4; ++j) y[j] = exp_diff(v[r][j], m) * inv;
             __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(yr) + i);
         }
     }
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(1024) void online_softmax_wide_kernel(const float *
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
-            MS o{__shfl_xor(st.sh, off, 64), __shfl_xor(st.s, off, 64)};
+            MS o{__shfl_xor(st.m, off, 64), __shfl_xor(st.s, off, 64)};
             st = merge(st, o);
         }
         if (lane == 0) part[wave] = st;
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(1024) void online_softmax_wide_kernel(const float *
 #pragma unroll
         for (int w = 1; w < 16; ++w) all = merge(all, part[w]);
         __syncthreads();  // part[] is rewritten by the next row
-        const float sh = all.sh;
+        const float m = all.m;
         const float inv = 1.f / all.s;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(1024) void online_softmax_wide_kernel(const float *
             if (i < nv) {
                 f32x4 o;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[r][j], LOG2E, -sh)) * inv;
+                for (int j = 0; j < 4; ++j) o[j] = exp_diff(v[r][j], m) * inv;
                 __builtin_nontemporal_store(o, yr + i);
             }
         }

@@ -158,3 +158,23 @@ def test_plan_rejects_like_attn_fwd(L):
         assert L.attn_fwd_plan(*args, ctypes.byref(splits)) is None, args
         assert splits.value == 0
     assert L.attn_fwd_plan(1, 1, 4, 4, 64, 1, 0, None) is not None
+
+
+def test_softmax_xent_validation(L, buf):
+    f = L.softmax_xent
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    assert f(buf, buf, buf, buf, buf, -1, 3, None) == SHAPE
+    assert f(buf, buf, buf, buf, buf, 2, -1, None) == SHAPE
+    assert f(buf, buf, buf, buf, buf, 2, 0, None) == SHAPE
+    assert f(None, buf, buf, None, None, 2, 3, None) == NULL
+    assert f(buf, None, buf, None, None, 2, 3, None) == NULL
+    assert f(buf, buf, None, None, None, 2, 3, None) == NULL
+    assert f(buf + 4, buf, buf, None, None, 2, 3, None) == ALIGN
+    assert f(buf, buf + 4, buf, None, None, 2, 3, None) == ALIGN
+    assert f(buf, buf, buf + 2, None, None, 2, 3, None) == ALIGN
+    assert f(buf, buf, buf, buf + 1, None, 2, 3, None) == ALIGN
+    assert f(buf, buf, buf, None, buf + 3, 2, 3, None) == ALIGN
+    assert f(buf, buf, buf, None, None, 1, 2**31, None) == OVERFLOW
+    assert f(buf, buf, buf, None, None, 2**40, 2**30, None) == OVERFLOW
+    assert f(None, None, None, None, None, 0, 5, None) == OK
+    assert f(None, None, None, None, None, 0, 0, None) == OK

@@ -71,6 +71,22 @@ def test_large_logits_and_neg_inf():
     assert np.all(y[2, ::3] == 0.0)
 
 
+@pytest.mark.parametrize("n", [300, 6000, 70000])
+def test_huge_logits(n):
+    # Logits far beyond any exponent range: only differences matter.
+    x = si.make_rows(5, n, seed=4, spread=1.0)
+    x[0, :] = -1e30                 # all equal and huge: uniform
+    x[1, :] = 3e37
+    x[2, :] = np.float32(1e30) * np.sign(x[2, :])  # two distinct values 2e30 apart: one-hot on the positive ones
+    x[3] *= np.float32(1e6)         # spread of a million
+    x[4, 7] = 1e38
+    log(f"[gpu] online_softmax huge logits n={n}")
+    y = gpu_softmax(x)
+    ref = oracle.softmax(x.astype(np.float64))
+    assert np.all(np.isfinite(y))
+    assert np.max(np.abs(y - ref)) <= F32_TOL
+
+
 def test_many_rows_and_in_place():
     import torch
 

@@ -1,0 +1,129 @@
+"""GPU parity of softmax_xent (through the C ABI) against the float64 oracle:
+per-row loss and LSE, the batch mean, the pages' worked example, labels at
+the row ends, invalid labels, large logits and every row width class."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from parity import F32_TOL, log
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def gpu_xent(x: np.ndarray, labels: np.ndarray):
+    import torch
+
+    import online_softmax_10_amd as osa
+
+    xd = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    ld = torch.from_numpy(np.ascontiguousarray(labels, dtype=np.int64)).cuda()
+    loss, lse, mean = osa.softmax_xent(xd, ld)
+    torch.cuda.synchronize()
+    return (loss.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+            float(mean.cpu().item()))
+
+
+def row_tol(x: np.ndarray) -> np.ndarray:
+    # Per row: fp32 rounding of the LSE grows with the row's largest finite
+    # logit (as for the fp32 attention bound: 1e-5 scaled by max|logit| / 8
+    # when above 8).
+    a = np.where(np.isfinite(x), np.abs(x), 0.0).max(axis=1)
+    return F32_TOL * np.maximum(1.0, a / 8.0)
+
+
+def check(x, labels, what):
+    loss, lse, mean = gpu_xent(x, labels)
+    ref_loss, ref_lse, ref_mean = oracle.cross_entropy(x.astype(np.float64), labels)
+    t = row_tol(x)
+    dl = np.abs(loss - ref_loss)
+    # The LSE of a row of huge logits is only as exact as its fp32 rounding.
+    ds = np.abs(lse - ref_lse) - 2.0 ** -23 * np.abs(ref_lse)
+    log(f"  {what}: max|dloss|={dl.max():.3e} max|dlse|={np.abs(lse - ref_lse).max():.3e} "
+        f"|dmean|={abs(mean - ref_mean):.3e} (tol {t.min():.1e}..{t.max():.1e})")
+    assert np.all(dl <= t), (dl.max(), t[np.argmax(dl - t)])
+    assert np.all(ds <= t), ds.max()
+    assert abs(mean - ref_mean) <= t.max() + 2.0 ** -23 * abs(ref_mean), (mean, ref_mean)
+
+
+def test_worked_example():
+    with open(os.path.join(GOLDEN, "w2_cross_entropy.json"), encoding="utf-8") as f:
+        g = json.load(f)
+    log("[gpu] softmax_xent on the worked-example logits")
+    x = np.array([g["logits"]], dtype=np.float32)
+    loss, lse, mean = gpu_xent(x, np.array([g["label"]]))
+    assert abs(loss[0] - g["loss"]) <= g["tol_printed"] and abs(mean - g["loss"]) <= g["tol_printed"]
+    check(x, np.array([g["label"]]), "worked example")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 64, 1000, 2048, 2049, 2052, 4096, 16384, 16385, 16388, 32000,
+                               65536, 100003])
+def test_rows_match_oracle(n):
+    rows = 41 if n <= 4096 else 7
+    x = si.make_rows(rows, n, seed=n, spread=4.0)
+    rng = np.random.default_rng(n + 1)
+    labels = rng.integers(0, n, size=rows)
+    labels[0], labels[-1] = 0, n - 1  # the row ends
+    log(f"[gpu] softmax_xent rows={rows} n={n}")
+    check(x, labels, f"n={n}")
+
+
+def test_many_rows_grid_stride():
+    # More rows than one grid pass of the one-wave kernel (65536 workgroups x 4 rows).
+    rows, n = 262147, 8
+    x = si.make_rows(rows, n, seed=5, spread=2.0)
+    labels = np.random.default_rng(6).integers(0, n, size=rows)
+    log(f"[gpu] softmax_xent rows={rows} n={n}")
+    check(x, labels, "grid stride")
+
+
+def test_large_logits_and_peaked_rows():
+    x = si.make_rows(9, 300, seed=3, spread=1.0)
+    x[0] += 1000.0                 # all large
+    x[1, 17] = 80.0                # one dominant logit, label on it
+    x[2, 5] = 80.0                 # dominant logit, label elsewhere
+    x[3, :] = -1e30                # all hugely negative
+    x[4, ::2] = -np.inf            # half masked
+    x[5, :] = 3e37                 # all equal and huge: log n
+    x[6] *= np.float32(1e6)        # spread of a million
+    labels = np.array([1, 17, 6, 0, 1, 2, 3, 4, 5])
+    log("[gpu] softmax_xent large / peaked / masked rows")
+    check(x, labels, "large logits")
+
+
+def test_invalid_labels_give_nan():
+    x = si.make_rows(4, 10, seed=9)
+    labels = np.array([-1, 10, 3, 12345678901])
+    log("[gpu] softmax_xent invalid labels")
+    loss, lse, mean = gpu_xent(x, labels)
+    assert math.isnan(loss[0]) and math.isnan(loss[1]) and math.isnan(loss[3]) and math.isnan(mean)
+    ref_loss, ref_lse, _ = oracle.cross_entropy(x.astype(np.float64), labels)
+    assert abs(loss[2] - ref_loss[2]) <= F32_TOL
+    assert np.max(np.abs(lse - ref_lse)) <= F32_TOL
+
+
+def test_empty_and_no_mean():
+    import torch
+
+    import online_softmax_10_amd as osa
+
+    log("[gpu] softmax_xent empty batch, mean=False")
+    x = torch.zeros((0, 7), dtype=torch.float32, device="cuda")
+    lab = torch.zeros((0,), dtype=torch.int64, device="cuda")
+    loss, lse, mean = osa.softmax_xent(x, lab)
+    torch.cuda.synchronize()
+    assert loss.shape == (0,) and lse.shape == (0,)
+    x = torch.zeros((3, 7), dtype=torch.float32, device="cuda")
+    lab = torch.tensor([0, 3, 6], dtype=torch.int64, device="cuda")
+    loss, lse, mean = osa.softmax_xent(x, lab, mean=False)
+    torch.cuda.synchronize()
+    assert mean is None and np.allclose(loss.cpu().numpy(), math.log(7), atol=1e-6)
+    with pytest.raises(ValueError):
+        osa.softmax_xent(x, lab[:2])
