@@ -52,11 +52,13 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_online_normalizer_f64.argtypes = [_f64p, _f64p, _f64p, _i64, _i64]
     lib.oracle_attn_rows_f64.argtypes = [_f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64,
                                          ctypes.c_double, ctypes.c_int, _i64p, _i64, _f64p, _f64p]
+    lib.oracle_attn_masked_rows_f64.argtypes = [_f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64,
+                                                ctypes.c_double, ctypes.c_int, _i64p, _i64p, _i64, _f64p, _f64p]
     lib.oracle_attn_f64.argtypes = [_f64p, _f64p, _f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64,
                                     ctypes.c_double, ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
     for name in ("oracle_softmax_f64", "oracle_logsumexp_f64", "oracle_xent_f64", "oracle_online_normalizer_f64",
-                 "oracle_attn_rows_f64", "oracle_attn_f64"):
+                 "oracle_attn_rows_f64", "oracle_attn_masked_rows_f64", "oracle_attn_f64"):
         getattr(lib, name).restype = None
     return lib
 
@@ -132,8 +134,16 @@ def online_normalizer(x, lib=None):
     return m, s
 
 
-def attention(q, k, v, scale: float, causal: bool, lib=None):
-    """Exact attention.  q [B,H,N,d], k/v [B,H,M,d] float64 -> (o [B,H,N,d], lse [B,H,N])."""
+def attention(q, k, v, scale: float, causal, lib=None, kv_len=None):
+    """Exact attention.  q [B,H,N,d], k/v [B,H,M,d] float64 -> (o [B,H,N,d], lse [B,H,N]).
+
+    causal and kv_len as in attention_rows.
+    """
+    if causal not in (False, True) or kv_len is not None:
+        q = _c64(q)
+        B, H, N, d = q.shape
+        o, lse = attention_rows(q, k, v, scale, causal, np.arange(B * H * N), lib, kv_len)
+        return o.reshape(B, H, N, d), lse.reshape(B, H, N)
     q, k, v = _c64(q), _c64(k), _c64(v)
     B, H, N, d = q.shape
     M = k.shape[2]
@@ -145,17 +155,27 @@ def attention(q, k, v, scale: float, causal: bool, lib=None):
     return o, lse
 
 
-def attention_rows(q, k, v, scale: float, causal: bool, rows, lib=None):
-    """Exact attention for flat rows r=(b*H+h)*N+i -> (o [len(rows), d], lse [len(rows)])."""
+def attention_rows(q, k, v, scale: float, causal, rows, lib=None, kv_len=None):
+    """Exact attention for flat rows r=(b*H+h)*N+i -> (o [len(rows), d], lse [len(rows)]).
+
+    causal: False / True (top-left: key j masked when j > i) / "bottom_right"
+    (key j masked when j > i + M - N).  kv_len: optional [B] valid key counts
+    (keys j >= kv_len[b] masked).  A row with no visible key gives o = 0,
+    lse = -inf.
+    """
     q, k, v = _c64(q), _c64(k), _c64(v)
     B, H, N, d = q.shape
     M = k.shape[2]
     assert k.shape == (B, H, M, d) and v.shape == (B, H, M, d) and M >= 1
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     assert rows.ndim == 1 and (rows.size == 0 or (rows.min() >= 0 and rows.max() < B * H * N))
+    mode = {False: 0, True: 1, "top_left": 1, "bottom_right": 2}[causal]
+    kl = None
+    if kv_len is not None:
+        kl = np.ascontiguousarray(np.asarray(kv_len, dtype=np.int64).reshape(B))
     o = np.empty((rows.size, d), dtype=np.float64)
     lse = np.empty(rows.size, dtype=np.float64)
-    (lib or load()).oracle_attn_rows_f64(_p(q), _p(k), _p(v), B, H, N, M, d, float(scale),
-                                         int(bool(causal)), rows.ctypes.data_as(_i64p), rows.size,
-                                         _p(o), _p(lse))
+    (lib or load()).oracle_attn_masked_rows_f64(_p(q), _p(k), _p(v), B, H, N, M, d, float(scale), mode,
+                                                kl.ctypes.data_as(_i64p) if kl is not None else None,
+                                                rows.ctypes.data_as(_i64p), rows.size, _p(o), _p(lse))
     return o, lse

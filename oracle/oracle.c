@@ -139,21 +139,27 @@ void oracle_online_normalizer_f64(const double *x, double *m_out, double *s_out,
  * three-pass safe softmax as above; LSE from the "softmax形式推导" section
  * of the "从原始Softmax到在线Softmax" page.
  *
- * mask(): with causal != 0, key j is masked for query i when j > i (key index
- * greater than query index, counted from 0 in both).  Otherwise no mask.
+ * mask() (the page leaves it open): key j of batch b is masked for query i
+ * when
+ *   - j >= kv_len[b]            (kv_len != NULL: the batch's valid key count),
+ *   - j > i                     (causal_mode 1: key index greater than query
+ *                                index, counted from 0 in both),
+ *   - j > i + (M - N)           (causal_mode 2: the same, aligned at the last
+ *                                query and the last key).
+ * The visible keys of a row are therefore a prefix [0, visible).  A row with
+ * no visible key has an empty sum: o = 0 and LSE = -inf.
  *
  * q: [B,H,N,d], k and v: [B,H,M,d], contiguous.  rows: flat indices
  * r = (b*H + h)*N + i.  Outputs: o_rows [nrows, d], lse_rows [nrows] (natural
- * log over the scaled, masked scores).  M >= 1 so every row sees key 0.
+ * log over the scaled, masked scores).
  */
-void oracle_attn_rows_f64(const double *q, const double *k, const double *v,
-                          int64_t B, int64_t H, int64_t N, int64_t M, int64_t d,
-                          double scale, int causal,
-                          const int64_t *rows, int64_t nrows,
-                          double *o_rows, double *lse_rows)
+void oracle_attn_masked_rows_f64(const double *q, const double *k, const double *v,
+                                 int64_t B, int64_t H, int64_t N, int64_t M, int64_t d,
+                                 double scale, int causal_mode, const int64_t *kv_len,
+                                 const int64_t *rows, int64_t nrows,
+                                 double *o_rows, double *lse_rows)
 {
     (void)B;
-    (void)H;
     int64_t t;
 #pragma omp parallel
     {
@@ -167,8 +173,18 @@ void oracle_attn_rows_f64(const double *q, const double *k, const double *v,
             const double *kh = k + bh * M * d;
             const double *vh = v + bh * M * d;
             double *oi = o_rows + t * d;
+            /* The visible keys of row i are a prefix [0, visible). */
             int64_t visible = M;
-            if (causal && i + 1 < M) visible = i + 1;
+            if (kv_len && kv_len[bh / H] < visible) visible = kv_len[bh / H] > 0 ? kv_len[bh / H] : 0;
+            if (causal_mode == 1 && i + 1 < visible) visible = i + 1;
+            if (causal_mode == 2 && i + 1 + (M - N) < visible) visible = i + 1 + (M - N) > 0 ? i + 1 + (M - N) : 0;
+            if (visible == 0) {
+                /* No visible key: an empty sum; o = 0 and LSE = log 0. */
+                for (int64_t c = 0; c < d; ++c)
+                    oi[c] = 0.0;
+                lse_rows[t] = -INFINITY;
+                continue;
+            }
 
             /* scores s_j = scale * <q_i, k_j> for the visible keys */
             for (int64_t j = 0; j < visible; ++j) {
@@ -197,6 +213,17 @@ void oracle_attn_rows_f64(const double *q, const double *k, const double *v,
         }
         free(s);
     }
+}
+
+/* No mask (causal = 0) or the top-left causal mask (causal != 0). */
+void oracle_attn_rows_f64(const double *q, const double *k, const double *v,
+                          int64_t B, int64_t H, int64_t N, int64_t M, int64_t d,
+                          double scale, int causal,
+                          const int64_t *rows, int64_t nrows,
+                          double *o_rows, double *lse_rows)
+{
+    oracle_attn_masked_rows_f64(q, k, v, B, H, N, M, d, scale, causal ? 1 : 0, NULL, rows, nrows, o_rows,
+                                lse_rows);
 }
 
 /* All rows of all heads: o [B,H,N,d], lse [B,H,N]. */

@@ -339,6 +339,69 @@ def pin_cross_entropy(lib):
     assert math.isnan(loss[0]) and math.isnan(loss[1]) and abs(loss[2] - math.log(4)) < 1e-12, loss
 
 
+def _torch_masked(q, k, v, scale, mode, kv_len):
+    """softmax(masked scores) V and LSE with torch float64, rows with a visible key only."""
+    import torch
+
+    qt, kt, vt = (torch.from_numpy(a) for a in (q, k, v))
+    B, H, N, d = q.shape
+    M = k.shape[2]
+    s = torch.matmul(qt, kt.transpose(-1, -2).contiguous()) * scale
+    i = torch.arange(N).view(N, 1)
+    j = torch.arange(M).view(1, M)
+    allow = torch.ones(B, 1, N, M, dtype=torch.bool)
+    if mode == "top_left":
+        allow &= (j <= i)
+    elif mode == "bottom_right":
+        allow &= (j <= i + (M - N))
+    if kv_len is not None:
+        allow &= (j.view(1, 1, 1, M) < torch.tensor(kv_len).view(B, 1, 1, 1))
+    s = s.masked_fill(~allow, float("-inf"))
+    any_visible = allow.expand(B, H, N, M).any(dim=-1)
+    p = torch.softmax(s, dim=-1)
+    o = torch.matmul(torch.nan_to_num(p, nan=0.0), vt)
+    lse = torch.logsumexp(s, dim=-1)
+    return o.numpy(), lse.numpy(), any_visible.numpy()
+
+
+def pin_attention_masks(lib):
+    # torch float64 with explicit boolean masks on small random problems.
+    cases = [(2, 2, 5, 9, 4, "bottom_right", None), (2, 2, 9, 5, 4, "bottom_right", None),
+             (2, 1, 7, 7, 3, "top_left", [3, 7]), (3, 2, 6, 11, 4, False, [0, 5, 11]),
+             (2, 2, 8, 6, 4, "bottom_right", [2, 6]), (1, 3, 4, 13, 5, "top_left", [9])]
+    for n, (B, H, N, M, d, mode, kl) in enumerate(cases):
+        q, k, v = _rand((B, H, N, d), 50 + n), _rand((B, H, M, d), 60 + n), _rand((B, H, M, d), 70 + n)
+        scale = 0.7
+        o, lse = oracle.attention(q, k, v, scale, mode, lib, kv_len=kl)
+        ro, rl, vis = _torch_masked(q, k, v, scale, mode, kl)
+        close(o[vis], ro[vis], 1e-12, f"masked attention O vs torch, case {n}")
+        close(lse[vis], rl[vis], 1e-12, f"masked attention LSE vs torch, case {n}")
+        assert np.all(o[~vis] == 0.0) and np.all(np.isneginf(lse[~vis])), f"empty rows, case {n}"
+    # Special cases that reduce to the plain definitions.
+    q, k, v = _rand((2, 2, 6, 4), 80), _rand((2, 2, 6, 4), 81), _rand((2, 2, 6, 4), 82)
+    o1, l1 = oracle.attention(q, k, v, 0.5, True, lib)
+    o2, l2 = oracle.attention(q, k, v, 0.5, "bottom_right", lib)
+    close(o2, o1, 0.0, "bottom-right = top-left when N = M")
+    close(l2, l1, 0.0, "bottom-right LSE = top-left LSE when N = M")
+    o3, l3 = oracle.attention(q, k, v, 0.5, False, lib, kv_len=[6, 6])
+    o4, l4 = oracle.attention(q, k, v, 0.5, False, lib)
+    close(o3, o4, 0.0, "key lengths of M = no key mask")
+    close(l3, l4, 0.0, "key lengths of M = no key mask (LSE)")
+    o5, l5 = oracle.attention(q, k, v, 0.5, False, lib, kv_len=[4, 2])
+    for b, L in enumerate((4, 2)):
+        ob, lb = oracle.attention(q[b:b + 1], k[b:b + 1, :, :L], v[b:b + 1, :, :L], 0.5, False, lib)
+        close(o5[b:b + 1], ob, 1e-14, f"key length {L} = keys sliced")
+        close(l5[b:b + 1], lb, 1e-14, f"key length {L} = keys sliced (LSE)")
+    # Bottom-right, N > M: the first N - M rows see no key.
+    q, k, v = _rand((1, 1, 7, 3), 90), _rand((1, 1, 4, 3), 91), _rand((1, 1, 4, 3), 92)
+    o, l = oracle.attention(q, k, v, 1.0, "bottom_right", lib)
+    assert np.all(o[0, 0, :3] == 0.0) and np.all(np.isneginf(l[0, 0, :3]))
+    for i in range(3, 7):
+        oi, li = oracle.attention(q[:, :, i:i + 1], k[:, :, :i - 2], v[:, :, :i - 2], 1.0, False, lib)
+        close(o[0, 0, i], oi[0, 0, 0], 1e-14, f"bottom-right row {i} = keys 0..{i - 3}")
+        close(l[0, 0, i], li[0, 0, 0], 1e-14, f"bottom-right row {i} LSE")
+
+
 ALL_PINS = [
     pin_w1_softmax,
     pin_w2_cross_entropy,
@@ -349,5 +412,6 @@ ALL_PINS = [
     pin_online_normalizer,
     pin_attention_brute_force,
     pin_attention_special_cases,
+    pin_attention_masks,
     pin_formulations_agree,
 ]

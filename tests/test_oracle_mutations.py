@@ -19,7 +19,15 @@ MUTATIONS = [
      "for (int64_t j = 0; j < visible; ++j)\n                l += exp(s[j] - m);",
      "for (int64_t j = 1; j < visible; ++j)\n                l += exp(s[j] - m);"),
     ("wrong sign in the weight", "double p = exp(s[j] - m) / l;", "double p = exp(m - s[j]) / l;"),
-    ("causal off by one", "if (causal && i + 1 < M) visible = i + 1;", "if (causal && i + 2 < M) visible = i + 2;"),
+    ("causal off by one", "if (causal_mode == 1 && i + 1 < visible) visible = i + 1;",
+     "if (causal_mode == 1 && i + 2 < visible) visible = i + 2;"),
+    ("bottom-right mask without the offset",
+     "if (causal_mode == 2 && i + 1 + (M - N) < visible) visible = i + 1 + (M - N) > 0 ? i + 1 + (M - N) : 0;",
+     "if (causal_mode == 2 && i + 1 < visible) visible = i + 1;"),
+    ("key lengths ignored", "if (kv_len && kv_len[bh / H] < visible)", "if (0 && kv_len && kv_len[bh / H] < visible)"),
+    ("key length of the wrong batch", "visible = kv_len[bh / H] > 0 ? kv_len[bh / H] : 0;",
+     "visible = kv_len[0] > 0 ? kv_len[0] : 0;"),
+    ("empty row LSE of 0", "lse_rows[t] = -INFINITY;", "lse_rows[t] = 0.0;"),
     ("K used in place of V", "oi[c] += p * vh[j * d + c];", "oi[c] += p * kh[j * d + c];"),
     ("reversed feature index", "acc += qi[c] * kh[j * d + c];", "acc += qi[c] * kh[j * d + (d - 1 - c)];"),
     ("LSE without the max", "lse_rows[t] = m + log(l);", "lse_rows[t] = log(l);"),
