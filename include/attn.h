@@ -40,7 +40,8 @@ enum {
     ATTN_ERR_OVERFLOW = -6,  /* sizes exceed the kernels' index range */
     ATTN_ERR_HIP = -7,       /* a HIP launch or allocation failed (see attn_last_error_detail) */
     ATTN_ERR_SCALE = -8,     /* scale is NaN or infinite */
-    ATTN_ERR_SPLITS = -9     /* num_splits outside [0, ATTN_MAX_SPLITS] */
+    ATTN_ERR_SPLITS = -9,    /* num_splits outside [0, ATTN_MAX_SPLITS] */
+    ATTN_ERR_MASK = -10      /* attn_mask.causal is not one of attn_causal */
 };
 
 /* Largest split count attn_fwd_splits accepts. */
@@ -110,6 +111,38 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 int attn_fwd_splits(const void *q, const void *k, const void *v, void *o, float *lse,
                     int64_t B, int64_t H, int64_t N, int64_t M, int d,
                     float scale, int causal, int dtype, int num_splits, void *stream);
+
+/*
+ * Masks for attn_fwd_masked.  The pages leave mask() open ("Online Softmax and
+ * Flash Attention" page, eq. (8)); these are the masks whose visible keys form
+ * a prefix of each row, so every row keeps the same online recurrence.
+ */
+typedef enum {
+    ATTN_CAUSAL_NONE = 0,         /* no causal mask */
+    ATTN_CAUSAL_TOP_LEFT = 1,     /* key j masked for query i when j > i (as attn_fwd's causal) */
+    ATTN_CAUSAL_BOTTOM_RIGHT = 2  /* key j masked when j > i + M - N: the last query sees every key */
+} attn_causal;
+
+typedef struct attn_mask {
+    int causal;             /* one of attn_causal */
+    const int32_t *kv_len;  /* [B] valid key count per batch (device, int32, 4-byte aligned): keys
+                               j >= kv_len[b] are masked (values clamped to [0, M]); NULL = M for all */
+} attn_mask;
+
+/*
+ * attn_fwd_masked -- attn_fwd_splits with a mask.
+ *
+ * The masks combine: key j of batch b is visible to query i when j < kv_len[b]
+ * and the causal rule (if any) allows it.  A query row with no visible key
+ * gets o = 0 and lse = -inf (an empty softmax sum).  mask == NULL means no mask.
+ *
+ * Arguments and errors as attn_fwd_splits, plus ATTN_ERR_MASK for an unknown
+ * causal mode and ATTN_ERR_ALIGN for a misaligned kv_len.  kv_len is read by
+ * the kernels (asynchronously, on `stream`); it is not validated on the host.
+ */
+int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int64_t B, int64_t H, int64_t N, int64_t M, int d,
+                    float scale, const attn_mask *mask, int dtype, int num_splits, void *stream);
 
 /*
  * online_softmax -- row-wise softmax with the one-pass normaliser.

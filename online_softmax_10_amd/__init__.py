@@ -16,7 +16,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_splits", "online_softmax", "softmax_xent", "plan", "lib", "LIB_PATH", "AttnError",
+__all__ = ["fwd", "fwd_splits", "online_softmax", "softmax_xent", "plan", "lib", "AttnMask", "CAUSAL_MODES", "LIB_PATH", "AttnError",
            "ATTN_F32", "ATTN_BF16", "ATTN_MAX_SPLITS", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -26,9 +26,17 @@ ATTN_BF16 = 1
 ATTN_MAX_SPLITS = 256
 ERROR_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
                -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_OVERFLOW", -7: "ATTN_ERR_HIP",
-               -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_SPLITS"}
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "online_softmax", "softmax_xent", "attn_fwd_plan",
-                    "attn_strerror", "attn_last_error_detail")
+               -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_SPLITS", -10: "ATTN_ERR_MASK"}
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "attn_fwd_masked", "online_softmax", "softmax_xent",
+                    "attn_fwd_plan", "attn_strerror", "attn_last_error_detail")
+
+# attn_causal of include/attn.h, by the names fwd() accepts.
+CAUSAL_MODES = {False: 0, True: 1, "none": 0, "top_left": 1, "bottom_right": 2}
+
+
+class AttnMask(ctypes.Structure):
+    """struct attn_mask of include/attn.h."""
+    _fields_ = [("causal", ctypes.c_int), ("kv_len", ctypes.c_void_p)]
 
 _lib = None
 
@@ -58,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_splits.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
         L.attn_fwd_splits.restype = ctypes.c_int
+        L.attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                      ctypes.POINTER(AttnMask), ctypes.c_int, ctypes.c_int, vp]
+        L.attn_fwd_masked.restype = ctypes.c_int
         L.online_softmax.argtypes = [vp, vp, i64, i64, vp]
         L.online_softmax.restype = ctypes.c_int
         L.attn_strerror.argtypes = [ctypes.c_int]
@@ -99,11 +110,15 @@ def _check_output(name, t, shape, dtype, device):
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
-def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None):
+def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None, kv_len=None):
     """Attention forward with an explicit split count (0 = library's choice).
 
     q [B,H,N,d], k and v [B,H,M,d]: contiguous CUDA/HIP tensors of one dtype
-    (bfloat16 or float32).  Returns (o [B,H,N,d] same dtype, lse [B,H,N] float32).
+    (bfloat16 or float32).  causal: False, True / "top_left" (key j masked for
+    query i when j > i) or "bottom_right" (when j > i + M - N).  kv_len:
+    optional contiguous int32 GPU tensor [B] of valid key counts (keys j >=
+    kv_len[b] masked).  Returns (o [B,H,N,d] same dtype, lse [B,H,N] float32);
+    a row with no visible key gets o = 0, lse = -inf.
     """
     import torch
 
@@ -131,17 +146,35 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
         _check_output("lse", lse, (B, H, N), torch.float32, q.device)
-    rc = lib().attn_fwd_splits(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                               B, H, N, M, d, float(scale), int(bool(causal)), code, int(num_splits),
+    if causal not in CAUSAL_MODES:
+        raise ValueError(f"causal must be one of {sorted(map(str, CAUSAL_MODES))}, got {causal!r}")
+    mode = CAUSAL_MODES[causal]
+    if kv_len is None and mode != 2:
+        rc = lib().attn_fwd_splits(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   B, H, N, M, d, float(scale), mode, code, int(num_splits),
+                                   _stream_handle(q.device))
+        if rc != 0:
+            raise AttnError(rc, "attn_fwd_splits")
+        return out, lse
+    if kv_len is not None:
+        if (kv_len.dtype != torch.int32 or kv_len.device != q.device or not kv_len.is_contiguous()
+                or kv_len.numel() != B):
+            raise ValueError(f"kv_len must be a contiguous int32 tensor of {B} entries on {q.device}")
+    mask = AttnMask(mode, kv_len.data_ptr() if kv_len is not None else None)
+    rc = lib().attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, N, M, d, float(scale), ctypes.byref(mask), code, int(num_splits),
                                _stream_handle(q.device))
     if rc != 0:
-        raise AttnError(rc, "attn_fwd_splits")
+        raise AttnError(rc, "attn_fwd_masked")
     return out, lse
 
 
-def fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
-    """softmax(mask(q k^T * scale)) v and the row log-sum-exp (natural log)."""
-    return fwd_splits(q, k, v, scale=scale, causal=causal, num_splits=0, out=out, lse=lse)
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None):
+    """softmax(mask(q k^T * scale)) v and the row log-sum-exp (natural log).
+
+    causal and kv_len as in fwd_splits.
+    """
+    return fwd_splits(q, k, v, scale=scale, causal=causal, num_splits=0, out=out, lse=lse, kv_len=kv_len)
 
 
 def plan(B, H, N, M, d, dtype="bf16", num_splits=0):

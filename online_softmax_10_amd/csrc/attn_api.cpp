@@ -71,8 +71,11 @@ Plan plan_for(int64_t BH, int64_t N, int64_t M, bool bf16, int num_splits) {
 }
 
 int validate_attn(const void *q, const void *k, const void *v, const void *o, const float *lse, int64_t B,
-                  int64_t H, int64_t N, int64_t M, int d, float scale, int dtype, int num_splits) {
+                  int64_t H, int64_t N, int64_t M, int d, float scale, int dtype, int num_splits,
+                  const attn_mask *mask) {
     if (B < 0 || H < 0 || N < 0 || M < 0) return ATTN_ERR_SHAPE;
+    if (mask && (mask->causal < ATTN_CAUSAL_NONE || mask->causal > ATTN_CAUSAL_BOTTOM_RIGHT)) return ATTN_ERR_MASK;
+    if (mask && mask->kv_len && (reinterpret_cast<uintptr_t>(mask->kv_len) & 3u)) return ATTN_ERR_ALIGN;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
     if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -112,8 +115,8 @@ const char *main_kernel_name(MainKernel k) {
 }
 
 int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H, int64_t N,
-             int64_t M, int d, float scale, int causal, int dtype, int num_splits, void *stream_v) {
-    const int rc = validate_attn(q, k, v, o, lse, B, H, N, M, d, scale, dtype, num_splits);
+             int64_t M, int d, float scale, const attn_mask *mask, int dtype, int num_splits, void *stream_v) {
+    const int rc = validate_attn(q, k, v, o, lse, B, H, N, M, d, scale, dtype, num_splits, mask);
     if (rc != ATTN_OK || B == 0 || H == 0 || N == 0) return rc;
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
     const bool bf16 = dtype == ATTN_BF16;
@@ -129,12 +132,16 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     p.N = (int)N;
     p.M = (int)M;
     p.d = d;
+    p.H = (int)H;
+    const int causal = mask ? mask->causal : ATTN_CAUSAL_NONE;
+    p.kv_len = mask ? mask->kv_len : nullptr;
+    p.causal_off = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? (int)(M - N) : 0;
     // Scores are kept in base-2 units.  c is at least the smallest normal float
     // so that a masked score (-inf) times c is -inf, never NaN; for scale = 0
     // this changes the (uniform) result by less than 2^-100 relative.
     p.c = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
     p.negate_q = signbit(scale) != 0;
-    p.causal = causal != 0;
+    p.causal = causal != ATTN_CAUSAL_NONE;
 
     const Plan plan = plan_for(BH, N, M, bf16, num_splits);
     const int64_t blocks = plan.kind == Plan::DECODE ? BH * plan.splits : BH * ceil_div(N, 128) * plan.splits;
@@ -191,12 +198,20 @@ extern "C" {
 
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H, int64_t N,
              int64_t M, int d, float scale, int causal, int dtype, void *stream) {
-    return run_attn(q, k, v, o, lse, B, H, N, M, d, scale, causal, dtype, 0, stream);
+    const attn_mask m{causal ? ATTN_CAUSAL_TOP_LEFT : ATTN_CAUSAL_NONE, nullptr};
+    return run_attn(q, k, v, o, lse, B, H, N, M, d, scale, &m, dtype, 0, stream);
 }
 
 int attn_fwd_splits(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
                     int64_t N, int64_t M, int d, float scale, int causal, int dtype, int num_splits, void *stream) {
-    return run_attn(q, k, v, o, lse, B, H, N, M, d, scale, causal, dtype, num_splits, stream);
+    const attn_mask m{causal ? ATTN_CAUSAL_TOP_LEFT : ATTN_CAUSAL_NONE, nullptr};
+    return run_attn(q, k, v, o, lse, B, H, N, M, d, scale, &m, dtype, num_splits, stream);
+}
+
+int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
+                    int64_t N, int64_t M, int d, float scale, const attn_mask *mask, int dtype, int num_splits,
+                    void *stream) {
+    return run_attn(q, k, v, o, lse, B, H, N, M, d, scale, mask, dtype, num_splits, stream);
 }
 
 int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stream) {
@@ -259,6 +274,7 @@ const char *attn_strerror(int code) {
     case ATTN_ERR_HIP: return "HIP launch or allocation failed";
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_SPLITS: return "num_splits outside [0, ATTN_MAX_SPLITS]";
+    case ATTN_ERR_MASK: return "unknown causal mode in attn_mask";
     default: return "unknown error code";
     }
 }

@@ -52,7 +52,8 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
                                           const uint16_t *__restrict__ v, uint16_t *__restrict__ o,
                                           float *__restrict__ lse, float *__restrict__ part_o,
                                           float *__restrict__ part_lse, int BH, int N, int M, float c,
-                                          uint32_t qsign, int ntq, int splits, int tiles_per_split) {
+                                          uint32_t qsign, int ntq, int splits, int tiles_per_split,
+                                          const int32_t *__restrict__ kv_len, int H, int coff) {
     using T = Tile<D>;
     constexpr int BR = 32 * NW;           // query rows per workgroup
     constexpr int LOADS = T::LOADS / NW;  // LDS-direct loads per wave per tile, for K and for V
@@ -79,15 +80,18 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     const int q0 = qt * BR;
 
     const int kb = sp * tiles_per_split * BC;
+    // Visible keys of this workgroup: its split's range, the batch's key
+    // length, and (causal) the last row's limit.
     int ke = min(M, kb + tiles_per_split * BC);
-    if (CAUSAL) ke = min(ke, q0 + BR);
+    if (kv_len != nullptr) ke = min(ke, max(kv_len[bh / H], 0));
+    if (CAUSAL) ke = min(ke, q0 + BR + coff);
     const int ntiles = ke > kb ? (ke - kb + BC - 1) / BC : 0;
 
     const u32x4 krs = make_rsrc(k + (size_t)bh * M * D, (uint32_t)M * T::RB);
     const u32x4 vrs = make_rsrc(v + (size_t)bh * M * D, (uint32_t)M * T::RB);
 
     WaveTile<D, CAUSAL> wt;
-    wt.init(q + (size_t)bh * N * D, N, q0 + wave * 32, lane, c, qsign);
+    wt.init(q + (size_t)bh * N * D, N, q0 + wave * 32, lane, c, qsign, coff);
 
     int ld_off[LOADS];
 #pragma unroll
@@ -204,8 +208,9 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,           \
         uint16_t *__restrict__ o, float *__restrict__ lse, float *__restrict__ part_o,                        \
         float *__restrict__ part_lse, int BH, int N, int M, float c, uint32_t qsign, int ntq, int splits,     \
-        int tiles_per_split
-#define ATTN_KERNEL_PASS q, k, v, o, lse, part_o, part_lse, BH, N, M, c, qsign, ntq, splits, tiles_per_split
+        int tiles_per_split, const int32_t *__restrict__ kv_len, int H, int coff
+#define ATTN_KERNEL_PASS \
+    q, k, v, o, lse, part_o, part_lse, BH, N, M, c, qsign, ntq, splits, tiles_per_split, kv_len, H, coff
 
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(ATTN_KERNEL_ARGS) {
@@ -227,7 +232,8 @@ hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * NW), 0, stream,
                        static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                        static_cast<const uint16_t *>(p.v), static_cast<uint16_t *>(p.o), p.lse, p.part_o,
-                       p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split);
+                       p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split, p.kv_len, p.H,
+                       p.causal_off);
     return hipGetLastError();
 }
 

@@ -147,13 +147,16 @@ struct WaveTile {
     int k_off[D / 16];    // K operand byte offsets (block cb adds 32 rows)
     int v_off[2][D / 32]; // V^T operand byte offsets (key chunk t4 adds 16 rows)
     int l32, hh, qrow, wq_lo;
+    int coff;  // causal offset: key j visible for query i iff j <= i + coff
     float c;
 
-    __device__ __forceinline__ void init(const uint16_t *qh, int N, int row0, int lane, float c_, uint32_t qsign) {
+    __device__ __forceinline__ void init(const uint16_t *qh, int N, int row0, int lane, float c_, uint32_t qsign,
+                                         int coff_) {
         l32 = lane & 31;
         hh = lane >> 5;
         wq_lo = row0;
         qrow = row0 + l32;
+        coff = coff_;
         c = c_;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
@@ -200,14 +203,14 @@ struct WaveTile {
     // Masked scores become -inf (then P is exactly 0).
     __device__ __forceinline__ void mask(int kv0, int ke, f32x16 (&s)[2]) const {
         // Accumulator register r of block cb holds key kv0 + 32*cb + 16*(r/8) + 8*hh + r%8.
-        const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > wq_lo);
+        const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > wq_lo + coff);
         if (need_mask) {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kv0 + 32 * cb + 16 * (r >> 3) + 8 * hh + (r & 7);
-                    const bool ok = key < ke && (!CAUSAL || key <= qrow);
+                    const bool ok = key < ke && (!CAUSAL || key <= qrow + coff);
                     s[cb][r] = ok ? s[cb][r] : NEG_INF;
                 }
         }

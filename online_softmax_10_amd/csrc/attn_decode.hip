@@ -68,7 +68,8 @@ template <int D, bool BF16, int NQ, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const void *__restrict__ qv, const void *__restrict__ kv,
                                                             const void *__restrict__ vv, float *__restrict__ part_o,
                                                             float *__restrict__ part_lse, int BH, int N, int M,
-                                                            float c, float qsign, int splits, int keys_per_split) {
+                                                            float c, float qsign, int splits, int keys_per_split,
+                                                            const int32_t *__restrict__ kv_len, int H, int coff) {
     using E = Elem<BF16>;
     constexpr int EPL = E::EPL;
     constexpr int LPK = D / EPL;      // lanes per key row
@@ -89,7 +90,8 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const void *__restri
     const int bh = blockIdx.x % BH;
     const int sp = blockIdx.x / BH;
     const int kb = sp * keys_per_split;
-    const int ke = min(M, kb + keys_per_split);
+    int ke = min(M, kb + keys_per_split);
+    if (kv_len != nullptr) ke = min(ke, max(kv_len[bh / H], 0));
 
     const char *qh = static_cast<const char *>(qv) + (size_t)bh * N * D * ESZ;
     const char *kh = static_cast<const char *>(kv) + (size_t)bh * M * D * ESZ;
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(NT, 2) void attn_decode_kernel(const void *__restri
 #pragma unroll
                 for (int i = 0; i < EPL; ++i) dot = __builtin_fmaf(qf[n][i], kf[u][i], dot);
                 dot = group_sum<LPK>(dot);
-                const bool ok = key[u] < ke && (!CAUSAL || key[u] <= n);
+                const bool ok = key[u] < ke && (!CAUSAL || key[u] <= n + coff);
                 s[u] = ok ? dot * c : NEG_INF;
                 mx = fmaxf(mx, s[u]);
             }
@@ -243,7 +245,7 @@ hipError_t launch_decode_t(const AttnProblem &p, hipStream_t stream) {
     const int keys_per_split = p.tiles_per_split * kDecodeKeyTile;
     hipLaunchKernelGGL((attn_decode_kernel<D, BF16, NQ, CAUSAL>), dim3((unsigned)((int64_t)p.BH * p.splits)),
                        dim3(NT), 0, stream, p.q, p.k, p.v, p.part_o, p.part_lse, p.BH, p.N, p.M, p.c,
-                       p.negate_q ? -1.f : 1.f, p.splits, keys_per_split);
+                       p.negate_q ? -1.f : 1.f, p.splits, keys_per_split, p.kv_len, p.H, p.causal_off);
     return hipGetLastError();
 }
 

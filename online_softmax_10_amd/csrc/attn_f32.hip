@@ -53,7 +53,8 @@ template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     float *__restrict__ o, float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
-    int BH, int N, int M, float c, float qsign, int ntq, int splits, int tiles_per_split) {
+    int BH, int N, int M, float c, float qsign, int ntq, int splits, int tiles_per_split,
+    const int32_t *__restrict__ kv_len, int H, int coff) {
     using Lay = Layout<D>;
     __shared__ __attribute__((aligned(16))) float Ks[BC * Lay::KS];
     __shared__ __attribute__((aligned(16))) float Vs[BC * Lay::VS];
@@ -75,7 +76,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
 
     const int kb = sp * tiles_per_split * BC;
     int ke = min(M, kb + tiles_per_split * BC);
-    if (CAUSAL) ke = min(ke, q0 + BR);
+    if (kv_len != nullptr) ke = min(ke, max(kv_len[bh / H], 0));
+    if (CAUSAL) ke = min(ke, q0 + BR + coff);
     const int ntiles = ke > kb ? (ke - kb + BC - 1) / BC : 0;
 
     const float *qh = q + (size_t)bh * N * D;
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
         stash();
         __syncthreads();
         if (t + 1 < ntiles) fetch(kv0 + BC);
-        if (CAUSAL && kv0 > wq_lo + 31) continue;
+        if (CAUSAL && kv0 > wq_lo + 31 + coff) continue;
 
         f32x16 s = f32x16{};
         const float *krow = &Ks[l32 * Lay::KS + hh];
@@ -136,12 +138,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
             s = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * kk], qop[kk], s, 0, 0, 0);
 
         // Register r holds key kv0 + 8*(r/4) + 4*hh + r%4.
-        const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > wq_lo);
+        const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > wq_lo + coff);
         if (need_mask) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kv0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool ok = key < ke && (!CAUSAL || key <= qrow);
+                const bool ok = key < ke && (!CAUSAL || key <= qrow + coff);
                 s[r] = ok ? s[r] : NEG_INF;
             }
         }
@@ -209,7 +211,8 @@ hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, SPLIT>), dim3((unsigned)blocks), dim3(NT), 0, stream,
                        static_cast<const float *>(p.q), static_cast<const float *>(p.k),
                        static_cast<const float *>(p.v), static_cast<float *>(p.o), p.lse, p.part_o, p.part_lse,
-                       p.BH, p.N, p.M, p.c, p.negate_q ? -1.f : 1.f, ntq, p.splits, p.tiles_per_split);
+                       p.BH, p.N, p.M, p.c, p.negate_q ? -1.f : 1.f, ntq, p.splits, p.tiles_per_split, p.kv_len,
+                       p.H, p.causal_off);
     return hipGetLastError();
 }
 

@@ -13,6 +13,9 @@ struct AttnProblem {
     void *o;                 // [BH,N,d] dtype (unused when writing partials)
     float *lse;              // [BH,N]          (unused when writing partials)
     int BH, N, M, d;
+    int H;                   // heads per batch (batch of head bh = bh / H)
+    const int32_t *kv_len;   // [B] valid keys per batch (device; clamped to [0, M]), or nullptr
+    int causal_off;          // causal: key j visible for query i iff j <= i + causal_off
     float c;                 // |scale| * log2(e): scores are kept in base-2 units
     bool negate_q;           // scale < 0: q's sign is flipped on load so c >= 0
     bool causal;

@@ -178,3 +178,19 @@ def test_softmax_xent_validation(L, buf):
     assert f(buf, buf, buf, None, None, 2**40, 2**30, None) == OVERFLOW
     assert f(None, None, None, None, None, 0, 5, None) == OK
     assert f(None, None, None, None, None, 0, 0, None) == OK
+
+
+def test_masked_validation(L, buf):
+    f = L.attn_fwd_masked
+    m = osa.AttnMask(3, None)
+    args = lambda mask, **kw: (buf, buf, buf, buf, buf, kw.get("B", 1), 1, 4, 4, 64, 0.125, mask, 1,
+                               kw.get("splits", 0), None)
+    assert f(*args(ctypes.byref(m))) == -10  # ATTN_ERR_MASK
+    m = osa.AttnMask(-1, None)
+    assert f(*args(ctypes.byref(m))) == -10
+    m = osa.AttnMask(2, buf + 2)
+    assert f(*args(ctypes.byref(m))) == ALIGN
+    m = osa.AttnMask(1, None)
+    assert f(*args(ctypes.byref(m), B=0)) == OK
+    assert f(*args(None, B=0)) == OK
+    assert f(*args(ctypes.byref(m), splits=-1)) == SPLITS
