@@ -241,6 +241,9 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--order", default="q_outer", choices=["q_outer", "kv_outer"],
+                    help="loop order of the attention: the fused query-outer kernels (default) or the "
+                         "key/value-outer order with the row state through HBM (attn_fwd_kv_outer)")
     ap.add_argument("--softmax", default="", metavar="ROWSxN",
                     help="instead of attention, time the row-wise online_softmax on a ROWS x N float32 matrix "
                          "(e.g. 32768x1024: the rows and key count of the 4x8x1024 workload)")
@@ -291,8 +294,12 @@ def main() -> int:
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=tdtype, device="cuda")
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
 
-    def step():
-        osa.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+    if args.order == "kv_outer":
+        def step():
+            osa.fwd_kv_outer(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+    else:
+        def step():
+            osa.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -322,6 +329,8 @@ def main() -> int:
         f"{value:.1f} TFLOP/s")
 
     kernel, splits = osa.plan(w.B, w.H, w.N, w.M, w.d, w.dtype)
+    if args.order == "kv_outer":
+        kernel, splits = "attn_kv_block_kernel (one launch per 64-key block)", 1
     achieved = w.flops / (launch_ms * 1e-3) / 1e12
     peak = PEAKS_TFLOPS[w.dtype]
     roofline = {
@@ -358,7 +367,8 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} M={w.M} d={w.d} {w.dtype} "
-                               f"{'causal' if w.causal else 'non-causal'}, seed {args.seed}",
+                               f"{'causal' if w.causal else 'non-causal'}, seed {args.seed}"
+                               + (", key/value-outer loop order" if args.order == "kv_outer" else ""),
                    "B": w.B, "H": w.H, "N": w.N, "M": w.M, "d": w.d, "causal": w.causal},
         "pct_of_bf16_peak": round(100.0 * value / PEAKS_TFLOPS["bf16"], 2),
         "roofline": roofline,

@@ -145,6 +145,24 @@ int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float 
                     float scale, const attn_mask *mask, int dtype, int num_splits, void *stream);
 
 /*
+ * attn_fwd_kv_outer -- the same attention as attn_fwd, computed in the
+ * key/value-outer loop order of the first FlashAttention formulation
+ * ("从原始Softmax到在线Softmax" page, the blocked online-softmax code under
+ * "softmax实际代码实现": key/value blocks outer, query blocks inner, each
+ * query block's normalised output, max and sum written back after every
+ * key/value block).  Provided to measure what the query-outer order of
+ * attn_fwd saves: per query tile and key block, the row state makes a round
+ * trip through HBM.  One kernel launch per 64-key block.
+ *
+ * Arguments as attn_fwd (causal = top-left); bf16 only (ATTN_ERR_DTYPE
+ * otherwise).  Allocates its fp32 row-state workspace (B*H*N*(d+2)*4 bytes)
+ * stream-ordered on `stream`.
+ */
+int attn_fwd_kv_outer(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int64_t B, int64_t H, int64_t N, int64_t M, int d,
+                      float scale, int causal, int dtype, void *stream);
+
+/*
  * online_softmax -- row-wise softmax with the one-pass normaliser.
  *
  * For each row r < rows of x [rows, n] (float32, row-major):

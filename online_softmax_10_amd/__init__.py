@@ -16,7 +16,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_splits", "online_softmax", "softmax_xent", "plan", "lib", "AttnMask", "CAUSAL_MODES", "LIB_PATH", "AttnError",
+__all__ = ["fwd", "fwd_splits", "fwd_kv_outer", "online_softmax", "softmax_xent", "plan", "lib", "AttnMask", "CAUSAL_MODES", "LIB_PATH", "AttnError",
            "ATTN_F32", "ATTN_BF16", "ATTN_MAX_SPLITS", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -27,8 +27,8 @@ ATTN_MAX_SPLITS = 256
 ERROR_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
                -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_OVERFLOW", -7: "ATTN_ERR_HIP",
                -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_SPLITS", -10: "ATTN_ERR_MASK"}
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "attn_fwd_masked", "online_softmax", "softmax_xent",
-                    "attn_fwd_plan", "attn_strerror", "attn_last_error_detail")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "attn_fwd_masked", "attn_fwd_kv_outer", "online_softmax",
+                    "softmax_xent", "attn_fwd_plan", "attn_strerror", "attn_last_error_detail")
 
 # attn_causal of include/attn.h, by the names fwd() accepts.
 CAUSAL_MODES = {False: 0, True: 1, "none": 0, "top_left": 1, "bottom_right": 2}
@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                       ctypes.POINTER(AttnMask), ctypes.c_int, ctypes.c_int, vp]
         L.attn_fwd_masked.restype = ctypes.c_int
+        L.attn_fwd_kv_outer.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_int, ctypes.c_int, vp]
+        L.attn_fwd_kv_outer.restype = ctypes.c_int
         L.online_softmax.argtypes = [vp, vp, i64, i64, vp]
         L.online_softmax.restype = ctypes.c_int
         L.attn_strerror.argtypes = [ctypes.c_int]
@@ -175,6 +178,42 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None):
     causal and kv_len as in fwd_splits.
     """
     return fwd_splits(q, k, v, scale=scale, causal=causal, num_splits=0, out=out, lse=lse, kv_len=kv_len)
+
+
+def fwd_kv_outer(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """The same attention in the key/value-outer loop order (row state through
+    HBM after every 64-key block); bf16 only.  For measuring loop orders."""
+    import torch
+
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("fwd_kv_outer takes bfloat16 q, k, v")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B,H,rows,d]")
+    B, H, N, d = q.shape
+    M = k.shape[2]
+    if tuple(k.shape) != (B, H, M, d) or tuple(v.shape) != (B, H, M, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous GPU tensor on q's device")
+    if causal not in (False, True):
+        raise ValueError("fwd_kv_outer supports causal=False or True (top-left)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    else:
+        _check_output("out", out, (B, H, N, d), q.dtype, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_output("lse", lse, (B, H, N), torch.float32, q.device)
+    rc = lib().attn_fwd_kv_outer(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                 B, H, N, M, d, float(scale), int(bool(causal)), ATTN_BF16,
+                                 _stream_handle(q.device))
+    if rc != 0:
+        raise AttnError(rc, "attn_fwd_kv_outer")
+    return out, lse
 
 
 def plan(B, H, N, M, d, dtype="bf16", num_splits=0):

@@ -214,6 +214,50 @@ int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float 
     return run_attn(q, k, v, o, lse, B, H, N, M, d, scale, mask, dtype, num_splits, stream);
 }
 
+int attn_fwd_kv_outer(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
+                      int64_t N, int64_t M, int d, float scale, int causal, int dtype, void *stream_v) {
+    const attn_mask m{causal ? ATTN_CAUSAL_TOP_LEFT : ATTN_CAUSAL_NONE, nullptr};
+    const int rc = validate_attn(q, k, v, o, lse, B, H, N, M, d, scale, dtype, 0, &m);
+    if (rc != ATTN_OK || B == 0 || H == 0 || N == 0) return rc;
+    if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    osa::AttnProblem p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.BH = (int)(B * H);
+    p.N = (int)N;
+    p.M = (int)M;
+    p.d = d;
+    p.H = (int)H;
+    p.c = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
+    p.negate_q = signbit(scale) != 0;
+    p.causal = causal != 0;
+    p.splits = 1;
+    const size_t rows = (size_t)B * H * N;
+    const size_t bytes = rows * (size_t)d * sizeof(float) + 2 * rows * sizeof(float);
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, bytes, stream);
+    if (e != hipSuccess) {
+        set_detail("hipMallocAsync of the row-state workspace", e);
+        return ATTN_ERR_HIP;
+    }
+    float *ws_o = static_cast<float *>(ws);
+    float *ws_m = ws_o + rows * (size_t)d;
+    float *ws_l = ws_m + rows;
+    e = osa::launch_attn_kv_outer(p, ws_o, ws_m, ws_l, stream);
+    if (e != hipSuccess) set_detail("key/value-outer kernel launch", e);
+    const hipError_t ef = hipFreeAsync(ws, stream);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+    if (ef != hipSuccess) {
+        set_detail("hipFreeAsync of the row-state workspace", ef);
+        return ATTN_ERR_HIP;
+    }
+    return ATTN_OK;
+}
+
 int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stream) {
     if (rows < 0 || n < 0) return ATTN_ERR_SHAPE;
     if (rows == 0) return ATTN_OK;

@@ -45,6 +45,10 @@ hipError_t launch_attn_decode(const AttnProblem &p, bool bf16, hipStream_t strea
 // lse = log sum_s e^{part_lse}, o = sum_s e^{part_lse - lse} part_o.
 hipError_t launch_split_merge(const AttnProblem &p, bool bf16, hipStream_t stream);
 
+// Key/value-outer loop order (one launch per key block, row state in the
+// fp32 workspace ws_o [BH,N,d], ws_m, ws_l [BH,N]); bf16, single pass, no mask
+// beyond top-left causal.
+hipError_t launch_attn_kv_outer(const AttnProblem &p, float *ws_o, float *ws_m, float *ws_l, hipStream_t stream);
 hipError_t launch_online_softmax(const float *x, float *y, int64_t rows, int64_t n, hipStream_t stream);
 // loss[i] = LSE_i - x[i, labels[i]] (NaN for a label outside [0, n)); lse and
 // mean optional (nullptr): the row LSE and the mean of the losses.
