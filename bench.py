@@ -11,10 +11,13 @@ stdout; progress goes to stderr.
              over the timed region
   roofline   the attention kernel against the bf16 dense MFMA peak
              (256 CUs x 2.4 GHz x 4096 flop/clk/CU = 2516.6 TFLOP/s); achieved
-             = algorithmic flops per launch / mean launch duration measured with
-             HIP events on the launch stream; traffic = HBM bytes per launch
-             from the committed rocprofv3 counter summary when it was taken on
-             the current kernel source, else null
+             = algorithmic flops per launch / the kernel's average launch
+             duration, measured with HIP events on the launch stream: the
+             timed region's duration / K (one launch of the kernel per step),
+             or the mean of per-launch event pairs with --launch-events;
+             traffic = HBM bytes per launch from the committed rocprofv3
+             counter summary when it was taken on the current kernel source,
+             else null
   cpu_baseline  the float64 oracle timed on this host's cores on a bounded,
              evenly spaced sample of the same workload's query rows
 """
@@ -241,6 +244,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch-events", action="store_true",
+                    help="also record an event pair around every step (adds a GPU drain per step)")
     ap.add_argument("--order", default="q_outer", choices=["q_outer", "kv_outer"],
                     help="loop order of the attention: the fused query-outer kernels (default) or the "
                          "key/value-outer order with the row state through HBM (attn_fwd_kv_outer)")
@@ -305,25 +310,36 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
+    # The timed region holds exactly K steps between two events on the launch
+    # stream.  Per-launch events (--launch-events) make the GPU drain and write
+    # a timestamp between kernels, which costs a few microseconds per step,
+    # so by default the kernel's average launch duration is the region's
+    # duration / K (each step is one launch of the dominant kernel; any gap
+    # between launches is counted, so it is an upper bound).
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] if args.launch_events else []
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] if args.launch_events else []
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_begin.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
+        if args.launch_events:
+            starts[i].record(stream)
         step()
-        ends[i].record(stream)
+        if args.launch_events:
+            ends[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
     total_ms = t_begin.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    if args.launch_events:
+        launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    else:
+        launch_ms = ms_per_step
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     err(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us), "
         f"{value:.1f} TFLOP/s")
@@ -343,6 +359,7 @@ def main() -> int:
         "kernel": kernel,
         "splits": splits,
         "launch_us": round(launch_ms * 1e3, 2),
+        "launch_timing": "per-launch event pairs" if args.launch_events else "timed region / steps",
         "algorithmic_bytes": algorithmic_bytes(w),
         "hbm_gbs_algorithmic": round(algorithmic_bytes(w) / (launch_ms * 1e-3) / 1e9, 1),
     }
