@@ -104,13 +104,15 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     };
 
     // On entry s_cur = S(j); after the barrier K(j+1) is in ks_next and V(j)
-    // in vs_cur.  FULL: tile j+1 exists (its scores go to s_nxt, and K(j+2),
-    // V(j+1) are loaded into the stages every wave has finished with).  Load
-    // tile indices past the last are clamped to it: a harmless reload into a
-    // free stage that keeps the block free of branches.
-    auto iteration = [&](auto full, int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const char *ks_next,
-                         char *ks_free, const char *vs_cur, char *vs_free) {
+    // in vs_cur.  FULL: this wave computes tile j+1 too (its scores go to
+    // s_nxt).  LOADS: tile j+1 exists for the workgroup, so this wave issues
+    // its share of K(j+2) and V(j+1) into the stages every wave has finished
+    // with.  Load tile indices past the last are clamped to it: a harmless
+    // reload into a free stage that keeps the block free of branches.
+    auto iteration = [&](auto full, auto loads, int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                         const char *ks_next, char *ks_free, const char *vs_cur, char *vs_free) {
         constexpr bool FULL = decltype(full)::value;
+        constexpr bool LOADS_ON = decltype(loads)::value;
         wait_loads_and_barrier<0>();
         wt.mask(kb + j * BC, ke, s_cur);
         const float m = wt.m_run;
@@ -137,7 +139,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
                 const int e = slot * (32 / SLOTS) + u;
                 wt.prob_pair(s_cur, e, m, popw, (e & 2) ? lsum1 : lsum0);
             }
-            if constexpr (FULL) {
+            if constexpr (LOADS_ON) {
                 if (slot % EVERY == EVERY - 1) {
                     load(krs, min(j + 2, ntiles - 1), ks_free, slot / EVERY);
                     load(vrs, j + 1, vs_free, slot / EVERY);
@@ -169,6 +171,23 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     };
     using Full = std::integral_constant<bool, true>;
     using Last = std::integral_constant<bool, false>;
+    using LoadsOn = std::integral_constant<bool, true>;
+    using LoadsOff = std::integral_constant<bool, false>;
+
+    // Tiles this wave computes: those holding a key visible to one of its
+    // rows (with a causal mask the last ones of the workgroup's range are
+    // fully masked for its first waves; rows past N need none).  Its
+    // remaining iterations only pass the barriers and issue its share of the
+    // loads, so every wave passes the same ntiles barriers.
+    int nw = 0;
+    {
+        const int row_lo = q0 + wave * 32;
+        const int row_hi = min(N, row_lo + 32) - 1;
+        int last_key = ke - 1;
+        if (CAUSAL) last_key = min(last_key, row_hi + coff);
+        if (row_hi >= row_lo && last_key >= kb) nw = (last_key - kb) / BC + 1;
+        nw = __builtin_amdgcn_readfirstlane(nw);
+    }
 
     if (ntiles > 0) {
         // Prologue: K(0), V(0) land; S(0) is computed while K(1) loads.
@@ -181,20 +200,40 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) load(krs, min(1, ntiles - 1), lds_k1, i);
         f32x16 sa[2] = {f32x16{}, f32x16{}}, sb[2];
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) wt.score_step(lds_k0, kk, sa);
         // Stages alternate with the parity of j: even j reads K(j+1) from k1
         // and V(j) from v0, and refills k0 and v1.
         int j = 0;
-        for (; j + 2 < ntiles; j += 2) {
-            iteration(Full{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
-            iteration(Full{}, j + 1, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+        if (nw > 0) {
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) wt.score_step(lds_k0, kk, sa);
+            for (; j + 2 < nw; j += 2) {
+                iteration(Full{}, LoadsOn{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+                iteration(Full{}, LoadsOn{}, j + 1, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+            }
+            // This wave's last tile: loads still go on while the workgroup has more.
+            if (j + 2 == nw) {
+                iteration(Full{}, LoadsOn{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+                ++j;
+                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+                else iteration(Last{}, LoadsOff{}, j, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+            } else {
+                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+                else iteration(Last{}, LoadsOff{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+            }
+            ++j;
         }
-        if (j + 2 == ntiles) {
-            iteration(Full{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
-            iteration(Last{}, j + 1, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
-        } else {
-            iteration(Last{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+        // Loads only, for the tiles other waves still compute.
+        for (; j < ntiles; ++j) {
+            wait_loads_and_barrier<0>();
+            if (j + 1 < ntiles) {
+                char *kdst = (j & 1) ? lds_k1 : lds_k0;
+                char *vdst = (j & 1) ? lds_v0 : lds_v1;
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    load(krs, min(j + 2, ntiles - 1), kdst, i);
+                    load(vrs, j + 1, vdst, i);
+                }
+            }
         }
         // The last iteration issues no loads and starts with a full wait, so
         // no LDS-direct load is in flight past this point.
