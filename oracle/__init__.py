@@ -53,7 +53,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_attn_rows_f64.argtypes = [_f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64,
                                          ctypes.c_double, ctypes.c_int, _i64p, _i64, _f64p, _f64p]
     lib.oracle_attn_masked_rows_f64.argtypes = [_f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64,
-                                                ctypes.c_double, ctypes.c_int, _i64p, _i64p, _i64, _f64p, _f64p]
+                                                ctypes.c_double, ctypes.c_int, _i64p, _f64p, _i64, _i64, _i64,
+                                                _i64p, _i64, _f64p, _f64p]
     lib.oracle_attn_f64.argtypes = [_f64p, _f64p, _f64p, _f64p, _f64p, _i64, _i64, _i64, _i64, _i64,
                                     ctypes.c_double, ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -134,15 +135,15 @@ def online_normalizer(x, lib=None):
     return m, s
 
 
-def attention(q, k, v, scale: float, causal, lib=None, kv_len=None):
+def attention(q, k, v, scale: float, causal, lib=None, kv_len=None, bias=None):
     """Exact attention.  q [B,H,N,d], k/v [B,H,M,d] float64 -> (o [B,H,N,d], lse [B,H,N]).
 
-    causal and kv_len as in attention_rows.
+    causal, kv_len and bias as in attention_rows.
     """
-    if causal not in (False, True) or kv_len is not None:
+    if causal not in (False, True) or kv_len is not None or bias is not None:
         q = _c64(q)
         B, H, N, d = q.shape
-        o, lse = attention_rows(q, k, v, scale, causal, np.arange(B * H * N), lib, kv_len)
+        o, lse = attention_rows(q, k, v, scale, causal, np.arange(B * H * N), lib, kv_len, bias)
         return o.reshape(B, H, N, d), lse.reshape(B, H, N)
     q, k, v = _c64(q), _c64(k), _c64(v)
     B, H, N, d = q.shape
@@ -155,13 +156,14 @@ def attention(q, k, v, scale: float, causal, lib=None, kv_len=None):
     return o, lse
 
 
-def attention_rows(q, k, v, scale: float, causal, rows, lib=None, kv_len=None):
+def attention_rows(q, k, v, scale: float, causal, rows, lib=None, kv_len=None, bias=None):
     """Exact attention for flat rows r=(b*H+h)*N+i -> (o [len(rows), d], lse [len(rows)]).
 
     causal: False / True (top-left: key j masked when j > i) / "bottom_right"
     (key j masked when j > i + M - N).  kv_len: optional [B] valid key counts
-    (keys j >= kv_len[b] masked).  A row with no visible key gives o = 0,
-    lse = -inf.
+    (keys j >= kv_len[b] masked).  bias: optional additive score bias
+    broadcastable to [B,H,N,M] (added after the scale; -inf masks a key).  A
+    row with no visible key, or only -inf scores, gives o = 0, lse = -inf.
     """
     q, k, v = _c64(q), _c64(k), _c64(v)
     B, H, N, d = q.shape
@@ -173,9 +175,15 @@ def attention_rows(q, k, v, scale: float, causal, rows, lib=None, kv_len=None):
     kl = None
     if kv_len is not None:
         kl = np.ascontiguousarray(np.asarray(kv_len, dtype=np.int64).reshape(B))
+    bp, bs = None, (0, 0, 0)
+    if bias is not None:
+        b64 = np.ascontiguousarray(bias, dtype=np.float64)
+        bv = np.broadcast_to(b64, (B, H, N, M))
+        assert bv.strides[3] == 8
+        bp, bs = _p(b64), tuple(st // 8 for st in bv.strides[:3])
     o = np.empty((rows.size, d), dtype=np.float64)
     lse = np.empty(rows.size, dtype=np.float64)
     (lib or load()).oracle_attn_masked_rows_f64(_p(q), _p(k), _p(v), B, H, N, M, d, float(scale), mode,
                                                 kl.ctypes.data_as(_i64p) if kl is not None else None,
-                                                rows.ctypes.data_as(_i64p), rows.size, _p(o), _p(lse))
+                                                bp, *bs, rows.ctypes.data_as(_i64p), rows.size, _p(o), _p(lse))
     return o, lse

@@ -149,6 +149,12 @@ void oracle_online_normalizer_f64(const double *x, double *m_out, double *s_out,
  * The visible keys of a row are therefore a prefix [0, visible).  A row with
  * no visible key has an empty sum: o = 0 and LSE = -inf.
  *
+ * Additive bias (optional; the elementwise mask() read as "add a term to
+ * each score"): s_ij = scale * <q_i, k_j> + bias[b*bias_sb + h*bias_sh +
+ * i*bias_sn + j], strides in elements, 0 to broadcast.  A bias of -inf masks
+ * its key; a row whose visible scores are all -inf is treated as one with no
+ * visible key.
+ *
  * q: [B,H,N,d], k and v: [B,H,M,d], contiguous.  rows: flat indices
  * r = (b*H + h)*N + i.  Outputs: o_rows [nrows, d], lse_rows [nrows] (natural
  * log over the scaled, masked scores).
@@ -156,6 +162,7 @@ void oracle_online_normalizer_f64(const double *x, double *m_out, double *s_out,
 void oracle_attn_masked_rows_f64(const double *q, const double *k, const double *v,
                                  int64_t B, int64_t H, int64_t N, int64_t M, int64_t d,
                                  double scale, int causal_mode, const int64_t *kv_len,
+                                 const double *bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sn,
                                  const int64_t *rows, int64_t nrows,
                                  double *o_rows, double *lse_rows)
 {
@@ -186,17 +193,28 @@ void oracle_attn_masked_rows_f64(const double *q, const double *k, const double 
                 continue;
             }
 
-            /* scores s_j = scale * <q_i, k_j> for the visible keys */
+            /* scores s_j = scale * <q_i, k_j> (+ bias_ij) for the visible keys */
+            const double *brow = bias ? bias + (bh / H) * bias_sb + (bh % H) * bias_sh + i * bias_sn : NULL;
             for (int64_t j = 0; j < visible; ++j) {
                 double acc = 0.0;
                 for (int64_t c = 0; c < d; ++c)
                     acc += qi[c] * kh[j * d + c];
                 s[j] = scale * acc;
+                if (brow)
+                    s[j] += brow[j];
             }
             /* pass 1: max */
             double m = s[0];
             for (int64_t j = 1; j < visible; ++j)
                 if (s[j] > m) m = s[j];
+            if (m == -INFINITY) {
+                /* Every visible score is -inf (a bias of -inf masks its key):
+                   as with no visible key. */
+                for (int64_t c = 0; c < d; ++c)
+                    oi[c] = 0.0;
+                lse_rows[t] = m;
+                continue;
+            }
             /* pass 2: sum of shifted exponentials */
             double l = 0.0;
             for (int64_t j = 0; j < visible; ++j)
@@ -222,8 +240,8 @@ void oracle_attn_rows_f64(const double *q, const double *k, const double *v,
                           const int64_t *rows, int64_t nrows,
                           double *o_rows, double *lse_rows)
 {
-    oracle_attn_masked_rows_f64(q, k, v, B, H, N, M, d, scale, causal ? 1 : 0, NULL, rows, nrows, o_rows,
-                                lse_rows);
+    oracle_attn_masked_rows_f64(q, k, v, B, H, N, M, d, scale, causal ? 1 : 0, NULL, NULL, 0, 0, 0, rows, nrows,
+                                o_rows, lse_rows);
 }
 
 /* All rows of all heads: o [B,H,N,d], lse [B,H,N]. */

@@ -402,6 +402,65 @@ def pin_attention_masks(lib):
         close(l[0, 0, i], li[0, 0, 0], 1e-14, f"bottom-right row {i} LSE")
 
 
+def pin_attention_bias(lib):
+    # Additive score bias: softmax(scale * Q K^T + bias) V.
+    import torch
+
+    rng = np.random.default_rng(95)
+    B, H, N, M, d = 2, 3, 5, 7, 4
+    q, k, v = _rand((B, H, N, d), 96), _rand((B, H, M, d), 97), _rand((B, H, M, d), 98)
+    bias = rng.standard_normal((B, H, N, M)) * 2.0
+    # Q = 0: the scores are the bias alone, so O is the e^bias-weighted mean of
+    # the values and LSE = log sum_j e^bias.
+    o, lse = oracle.attention(np.zeros_like(q), k, v, 0.7, False, lib, bias=bias)
+    w = np.exp(bias)
+    close(o, np.einsum("bhij,bhjd->bhid", w, v) / w.sum(-1, keepdims=True), 1e-14, "bias-only weights")
+    close(lse, np.log(w.sum(-1)), 1e-14, "bias-only LSE")
+    # A constant per row changes nothing but the LSE, by that constant.
+    o0, l0 = oracle.attention(q, k, v, 0.7, False, lib)
+    row_c = rng.standard_normal((B, H, N, 1)) * 5.0
+    o1, l1 = oracle.attention(q, k, v, 0.7, False, lib, bias=np.broadcast_to(row_c, (B, H, N, M)))
+    close(o1, o0, 1e-13, "row-constant bias leaves O")
+    close(l1, l0 + row_c[..., 0], 1e-13, "row-constant bias shifts LSE")
+    # -inf on keys >= L_b is the key-length mask.
+    L = [3, 7]
+    neg = np.zeros((B, H, N, M))
+    for b, Lb in enumerate(L):
+        neg[b, :, :, Lb:] = -np.inf
+    o2, l2 = oracle.attention(q, k, v, 0.7, "bottom_right", lib, bias=neg)
+    o3, l3 = oracle.attention(q, k, v, 0.7, "bottom_right", lib, kv_len=L)
+    close(o2, o3, 0.0, "-inf bias = key lengths")
+    close(l2, l3, 0.0, "-inf bias = key lengths (LSE)")
+    # A bias broadcast over batch and heads = the same bias written out.
+    b2 = rng.standard_normal((N, M))
+    o4, l4 = oracle.attention(q, k, v, 0.7, True, lib, bias=b2)
+    o5, l5 = oracle.attention(q, k, v, 0.7, True, lib, bias=np.ascontiguousarray(np.broadcast_to(b2, (B, H, N, M))))
+    close(o4, o5, 0.0, "broadcast bias = expanded bias")
+    close(l4, l5, 0.0, "broadcast bias = expanded bias (LSE)")
+    # A row whose scores are all -inf: o = 0, LSE = -inf; the other rows as
+    # with that row's bias absent.
+    b3 = bias.copy()
+    b3[1, 2, 3, :] = -np.inf
+    o6, l6 = oracle.attention(q, k, v, 0.7, False, lib, bias=b3)
+    o7, l7 = oracle.attention(q, k, v, 0.7, False, lib, bias=bias)
+    assert np.all(o6[1, 2, 3] == 0.0) and np.isneginf(l6[1, 2, 3]), "all -inf row"
+    keep = np.ones((B, H, N), dtype=bool)
+    keep[1, 2, 3] = False
+    close(o6[keep], o7[keep], 0.0, "other rows unchanged by one -inf row")
+    # torch float64 brute force, with the causal masks.
+    for mode in (True, "bottom_right"):
+        o8, l8 = oracle.attention(q, k, v, 0.7, mode, lib, bias=bias)
+        s = 0.7 * torch.matmul(torch.from_numpy(q), torch.from_numpy(k).transpose(-1, -2).contiguous())
+        s = s + torch.from_numpy(bias)
+        i = torch.arange(N)[:, None]
+        j = torch.arange(M)[None, :]
+        off = 0 if mode is True else M - N
+        s = s.masked_fill(j > i + off, float("-inf"))
+        ro = torch.matmul(torch.softmax(s, -1), torch.from_numpy(v))
+        close(o8, ro.numpy(), 1e-13, f"biased attention vs torch ({mode})")
+        close(l8, torch.logsumexp(s, -1).numpy(), 1e-13, f"biased LSE vs torch ({mode})")
+
+
 ALL_PINS = [
     pin_w1_softmax,
     pin_w2_cross_entropy,
@@ -413,5 +472,6 @@ ALL_PINS = [
     pin_attention_brute_force,
     pin_attention_special_cases,
     pin_attention_masks,
+    pin_attention_bias,
     pin_formulations_agree,
 ]

@@ -28,6 +28,11 @@ MUTATIONS = [
     ("key length of the wrong batch", "visible = kv_len[bh / H] > 0 ? kv_len[bh / H] : 0;",
      "visible = kv_len[0] > 0 ? kv_len[0] : 0;"),
     ("empty row LSE of 0", "lse_rows[t] = -INFINITY;", "lse_rows[t] = 0.0;"),
+    ("bias subtracted", "s[j] += brow[j];", "s[j] -= brow[j];"),
+    ("bias scaled with the product", "s[j] += brow[j];", "s[j] += scale * brow[j];"),
+    ("bias of head 0 for every head", "(bh % H) * bias_sh", "0 * bias_sh"),
+    ("bias rows of query 0", "i * bias_sn : NULL;", "0 * bias_sn : NULL;"),
+    ("all -inf row not caught", "if (m == -INFINITY) {", "if (0) {"),
     ("K used in place of V", "oi[c] += p * vh[j * d + c];", "oi[c] += p * kh[j * d + c];"),
     ("reversed feature index", "acc += qi[c] * kh[j * d + c];", "acc += qi[c] * kh[j * d + (d - 1 - c)];"),
     ("LSE without the max", "lse_rows[t] = m + log(l);", "lse_rows[t] = log(l);"),
