@@ -69,12 +69,75 @@ def load_traffic(workload: str, kernel: str):
     return t.get("hbm_bytes_per_launch")
 
 
+COPY_MIB = 512  # size of the plain copy that calibrates the byte counters
+
+
+def counter_commands(wl: str) -> list:
+    """The four rocprofv3 counter runs (from the repository root) that
+    --traffic-from-counters reads back."""
+    run = f"python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline"
+    cal = f"python3 bench.py --calibrate-copy {COPY_MIB} --steps 3"
+    return [f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_{wl} -o run -- {run}",
+            f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_{wl} -o run -- {run}",
+            f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_copy -o run -- {cal}",
+            f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o run -- {cal}"]
+
+
+def traffic_from_counters(wl: str, kernel: str, out_dir: str) -> dict:
+    """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE runs (KiB
+    per dispatch, first dispatch dropped), each scaled by what the same counter
+    reads for a plain copy of known size; written to
+    profiles/traffic_attn_fwd_<wl>.json with the current kernel-source hash."""
+    import collections
+    import csv
+    import glob
+
+    def per_dispatch(sub, match):
+        path = glob.glob(os.path.join(out_dir, sub, "**", "*counter_collection.csv"), recursive=True)[0]
+        per = collections.defaultdict(float)
+        with open(path, newline="", encoding="utf-8") as f:
+            for r in csv.DictReader(f):
+                if match(r["Kernel_Name"]):
+                    per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+        return [per[key] for key in sorted(per)]
+
+    is_kernel = lambda name: (kernel + "<") in name
+    is_copy = lambda name: "copyBuffer" in name
+    fetch = per_dispatch(f"pmc_fetch_{wl}", is_kernel)[1:]
+    write = per_dispatch(f"pmc_write_{wl}", is_kernel)[1:]
+    cf = per_dispatch("pmc_fetch_copy", is_copy)
+    cw = per_dispatch("pmc_write_copy", is_copy)
+    if not (fetch and write and cf and cw):
+        raise RuntimeError("counter runs hold no dispatches of the expected kernels")
+    copy_kib = COPY_MIB * 1024
+    ff = copy_kib / (sum(cf) / len(cf))
+    fw = copy_kib / (sum(cw) / len(cw))
+    fk = sum(fetch) / len(fetch)
+    wk = sum(write) / len(write)
+    out = {
+        "workload": wl,
+        "kernel": kernel,
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_kib_per_dispatch": round(fk, 1),
+        "write_kib_per_dispatch": round(wk, 1),
+        "copy_calibration": {"bytes": copy_kib * 1024, "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
+        "hbm_bytes_per_launch": round((fk * ff + wk * fw) * 1024),
+        "commands": counter_commands(wl) + [f"python3 bench.py --workload {wl} --traffic-from-counters gpurun_out"],
+        "note": "KiB per dispatch averaged over the timed dispatches (first excluded); factors = copied bytes / "
+                "counter bytes for a plain device copy",
+    }
+    with open(os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{wl}.json"), "w", encoding="utf-8") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def algorithmic_bytes(w: si.Workload) -> float:
     esz = 2 if w.dtype == "bf16" else 4
     return w.B * w.H * ((w.N + 2 * w.M) * w.d * esz + w.N * w.d * esz + w.N * 4)
 
 
-def cpu_baseline(w: si.Workload, q, k, v, o_gpu, lse_gpu, target_s: float):
+def cpu_baseline(w: si.Workload, q, k, v, o_gpu, lse_gpu, target_s: float, bias=None):
     """Time the oracle on an evenly spaced sample of query rows (~target_s seconds)."""
     import oracle
 
@@ -89,7 +152,7 @@ def cpu_baseline(w: si.Workload, q, k, v, o_gpu, lse_gpu, target_s: float):
 
     def run(rows):
         t0 = time.perf_counter()
-        o, lse = oracle.attention_rows(qf, kf, vf, w.scale, w.causal, rows)
+        o, lse = oracle.attention_rows(qf, kf, vf, w.scale, w.causal, rows, bias=bias)
         return time.perf_counter() - t0, o, lse
 
     probe = np.linspace(0, total - 1, 256).astype(np.int64)
@@ -115,15 +178,28 @@ def cpu_baseline(w: si.Workload, q, k, v, o_gpu, lse_gpu, target_s: float):
 
 
 def bench_softmax(args, torch, osa) -> int:
-    """online_softmax at bandwidth scale: one read and one write of the matrix per step."""
+    """online_softmax at bandwidth scale: one read and one write of the matrix per
+    step (--softmax-out y), plus the row LSE (y+lse), or the row LSE alone, one
+    read of the matrix (lse)."""
     import oracle
 
     rows, n = (int(t) for t in args.softmax.lower().split("x"))
     x_host = si.make_rows(rows, n, seed=args.seed, spread=4.0)
     x = torch.from_numpy(x_host).cuda()
-    y = torch.empty_like(x)
+    mode = args.softmax_out
+    y = torch.empty_like(x) if mode != "lse" else None
+    lse = torch.empty((rows,), dtype=torch.float32, device="cuda") if mode != "y" else None
+
+    def step():
+        if mode == "y":
+            osa.online_softmax(x, out=y)
+        elif mode == "y+lse":
+            osa.online_softmax(x, out=y, return_lse=True, lse=lse)
+        else:
+            osa.logsumexp(x, out=lse)
+
     for _ in range(args.warmup):
-        osa.online_softmax(x, out=y)
+        step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -132,23 +208,30 @@ def bench_softmax(args, torch, osa) -> int:
     t0.record(stream)
     for i in range(args.steps):
         starts[i].record(stream)
-        osa.online_softmax(x, out=y)
+        step()
         ends[i].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
-    nbytes = 2.0 * rows * n * 4  # x read once, y written once
+    # x read once; y written once; 4 bytes per row of LSE.
+    nbytes = (rows * n * 4.0) * (1 if mode == "lse" else 2) + (rows * 4.0 if mode != "y" else 0.0)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
     # Oracle on evenly spaced rows (bounded), also the parity spot check.
     sample = np.linspace(0, rows - 1, min(rows, max(2048, (1 << 26) // n))).astype(np.int64)
+    xs = x_host[sample].astype(np.float64)
     tc = time.perf_counter()
-    ref = oracle.softmax(x_host[sample].astype(np.float64))
+    ref = oracle.softmax(xs) if mode != "lse" else None
+    ref_lse = oracle.logsumexp(xs) if mode != "y" else None
     dt = time.perf_counter() - tc
-    err_max = float(np.max(np.abs(y.cpu().numpy()[sample].astype(np.float64) - ref)))
+    err_max = {}
+    if y is not None:
+        err_max["y"] = float(np.max(np.abs(y.cpu().numpy()[sample].astype(np.float64) - ref)))
+    if lse is not None:
+        err_max["lse"] = float(np.max(np.abs(lse.cpu().numpy()[sample].astype(np.float64) - ref_lse)))
     line = {
-        "metric": "online_softmax GB/s at 1 GPU",
+        "metric": "online_softmax GB/s at 1 GPU" if mode == "y" else f"online_softmax ({mode}) GB/s at 1 GPU",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -160,12 +243,13 @@ def bench_softmax(args, torch, osa) -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"online_softmax rows={rows} n={n} float32, N(0, 4^2) logits, seed {args.seed}",
-                   "rows": rows, "n": n},
+        "config": {"workload": f"online_softmax rows={rows} n={n} float32, N(0, 4^2) logits, seed {args.seed}, "
+                               f"outputs {mode}",
+                   "rows": rows, "n": n, "outputs": mode},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel": "online_softmax",
                      "launch_us": round(launch_ms * 1e3, 2), "algorithmic_bytes": nbytes},
-        "cpu_baseline": {"value": round(2.0 * len(sample) * n * 4 / dt / 1e9, 3), "unit": "GB/s",
+        "cpu_baseline": {"value": round(nbytes * len(sample) / rows / dt / 1e9, 3), "unit": "GB/s",
                          "cores": oracle.num_threads(),
                          "kind": "oracle", "sample": f"{len(sample)} of {rows} rows, evenly spaced ({dt:.2f} s)"},
         "max_abs_err_vs_oracle": err_max,
@@ -249,15 +333,29 @@ def main() -> int:
     ap.add_argument("--order", default="q_outer", choices=["q_outer", "kv_outer"],
                     help="loop order of the attention: the fused query-outer kernels (default) or the "
                          "key/value-outer order with the row state through HBM (attn_fwd_kv_outer)")
+    ap.add_argument("--bias", action="store_true",
+                    help="attention with an additive [N,M] float32 score bias broadcast over batch and heads")
     ap.add_argument("--softmax", default="", metavar="ROWSxN",
                     help="instead of attention, time the row-wise online_softmax on a ROWS x N float32 matrix "
                          "(e.g. 32768x1024: the rows and key count of the 4x8x1024 workload)")
+    ap.add_argument("--softmax-out", default="y", choices=["y", "y+lse", "lse"],
+                    help="with --softmax: the outputs written (softmax rows, rows and their LSE, or the LSE alone)")
     ap.add_argument("--xent", default="", metavar="ROWSxN",
                     help="instead of attention, time softmax_xent (per-row cross-entropy + mean) on ROWS x N "
                          "float32 logits (e.g. 8192x32000)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--traffic-from-counters", default="", metavar="DIR",
+                    help="no GPU work: read the FETCH_SIZE / WRITE_SIZE counter runs of --workload and of the "
+                         "copy calibration under DIR and write profiles/traffic_attn_fwd_<workload>.json")
     args = ap.parse_args()
+    if args.traffic_from_counters:
+        import online_softmax_10_amd as osa
+
+        w = si.WORKLOADS[args.workload]
+        kernel = osa.plan(w.B, w.H, w.N, w.M, w.d, w.dtype)[0]
+        print(json.dumps(traffic_from_counters(args.workload, kernel, args.traffic_from_counters), indent=1))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -285,6 +383,9 @@ def main() -> int:
         return bench_softmax(args, torch, osa)
     if args.xent:
         return bench_xent(args, torch, osa)
+    if args.bias and args.order == "kv_outer":
+        print("--bias applies to the fused (query-outer) kernels only.", file=sys.stderr)
+        return 2
     w = si.WORKLOADS[args.workload]
     err(f"[bench] workload {w}")
     q, k, v = si.make_qkv(w, args.seed)
@@ -299,9 +400,17 @@ def main() -> int:
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=tdtype, device="cuda")
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
 
+    bias_host = bias_dev = None
+    if args.bias:
+        # [N, M] float32 bias broadcast over batch and heads.
+        bias_host = si.make_bias((w.N, w.M), args.seed + 100)
+        bias_dev = torch.from_numpy(bias_host).cuda()
     if args.order == "kv_outer":
         def step():
             osa.fwd_kv_outer(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
+    elif args.bias:
+        def step():
+            osa.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, bias=bias_dev)
     else:
         def step():
             osa.fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse)
@@ -347,6 +456,10 @@ def main() -> int:
     kernel, splits = osa.plan(w.B, w.H, w.N, w.M, w.d, w.dtype)
     if args.order == "kv_outer":
         kernel, splits = "attn_kv_block_kernel (one launch per 64-key block)", 1
+    abytes = algorithmic_bytes(w)
+    if args.bias:
+        kernel = "attn_fwd_bf16_bias_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel"
+        abytes += w.N * w.M * 4  # the broadcast bias, read once
     achieved = w.flops / (launch_ms * 1e-3) / 1e12
     peak = PEAKS_TFLOPS[w.dtype]
     roofline = {
@@ -355,20 +468,21 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": load_traffic(w.name, kernel) if splits == 1 else None,
+        "traffic": load_traffic(w.name, kernel) if splits == 1 and not args.bias else None,
         "kernel": kernel,
         "splits": splits,
         "launch_us": round(launch_ms * 1e3, 2),
         "launch_timing": "per-launch event pairs" if args.launch_events else "timed region / steps",
-        "algorithmic_bytes": algorithmic_bytes(w),
-        "hbm_gbs_algorithmic": round(algorithmic_bytes(w) / (launch_ms * 1e-3) / 1e9, 1),
+        "algorithmic_bytes": abytes,
+        "hbm_gbs_algorithmic": round(abytes / (launch_ms * 1e-3) / 1e9, 1),
     }
 
     cpu = None
     if not args.no_cpu_baseline:
         o_host = o.float().cpu().numpy().astype(np.float64)
         l_host = lse.cpu().numpy().astype(np.float64)
-        cpu = cpu_baseline(w, q, k, v, o_host, l_host, args.cpu_seconds)
+        cpu = cpu_baseline(w, q, k, v, o_host, l_host, args.cpu_seconds,
+                           None if bias_host is None else bias_host.astype(np.float64))
 
     line = {
         "metric": "attn fwd TFLOP/s at 1 GPU + % of MI355X bf16 MFMA peak",
@@ -385,7 +499,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} M={w.M} d={w.d} {w.dtype} "
                                f"{'causal' if w.causal else 'non-causal'}, seed {args.seed}"
-                               + (", key/value-outer loop order" if args.order == "kv_outer" else ""),
+                               + (", key/value-outer loop order" if args.order == "kv_outer" else "")
+                               + (", additive [N,M] fp32 bias N(0, 2^2) broadcast over batch and heads"
+                                  if args.bias else ""),
                    "B": w.B, "H": w.H, "N": w.N, "M": w.M, "d": w.d, "causal": w.causal},
         "pct_of_bf16_peak": round(100.0 * value / PEAKS_TFLOPS["bf16"], 2),
         "roofline": roofline,

@@ -114,8 +114,10 @@ int attn_fwd_splits(const void *q, const void *k, const void *v, void *o, float 
 
 /*
  * Masks for attn_fwd_masked.  The pages leave mask() open ("Online Softmax and
- * Flash Attention" page, eq. (8)); these are the masks whose visible keys form
- * a prefix of each row, so every row keeps the same online recurrence.
+ * Flash Attention" page, eq. (8)).  Two kinds: masks whose visible keys form
+ * a prefix of each row (causal alignments, key lengths), and an additive
+ * score bias, the elementwise reading of mask(): the score of query i and
+ * key j becomes scale * <q_i, k_j> + bias_ij, and a bias of -inf masks.
  */
 typedef enum {
     ATTN_CAUSAL_NONE = 0,         /* no causal mask */
@@ -127,18 +129,30 @@ typedef struct attn_mask {
     int causal;             /* one of attn_causal */
     const int32_t *kv_len;  /* [B] valid key count per batch (device, int32, 4-byte aligned): keys
                                j >= kv_len[b] are masked (values clamped to [0, M]); NULL = M for all */
+    const float *bias;      /* additive score bias, fp32 (device, 16-byte aligned), or NULL: the
+                               bias of (b, h, i, j) is bias[b*bias_stride_b + h*bias_stride_h +
+                               i*bias_stride_n + j], j < M contiguous.  Values finite or -inf. */
+    int64_t bias_stride_b;  /* strides in elements: >= 0 (0 broadcasts) and multiples of 4 */
+    int64_t bias_stride_h;
+    int64_t bias_stride_n;
 } attn_mask;
 
 /*
  * attn_fwd_masked -- attn_fwd_splits with a mask.
  *
  * The masks combine: key j of batch b is visible to query i when j < kv_len[b]
- * and the causal rule (if any) allows it.  A query row with no visible key
- * gets o = 0 and lse = -inf (an empty softmax sum).  mask == NULL means no mask.
+ * and the causal rule (if any) allows it; the visible scores get the bias
+ * added.  A query row with no visible key, or whose visible scores are all
+ * -inf, gets o = 0 and lse = -inf (an empty softmax sum).  lse is taken over
+ * the biased scores.  mask == NULL means no mask.
  *
  * Arguments and errors as attn_fwd_splits, plus ATTN_ERR_MASK for an unknown
- * causal mode and ATTN_ERR_ALIGN for a misaligned kv_len.  kv_len is read by
- * the kernels (asynchronously, on `stream`); it is not validated on the host.
+ * causal mode, ATTN_ERR_ALIGN for a misaligned kv_len or bias (pointer or a
+ * stride not a multiple of 4) and ATTN_ERR_SHAPE for a negative bias stride.
+ * kv_len and bias are read by the kernels (asynchronously, on `stream`); they
+ * are not validated on the host.  Calls with a bias run on the four-wave bf16
+ * kernel (or the fp32 kernel), never the decode or eight-wave kernels, and
+ * attn_fwd_plan does not describe them.
  */
 int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse,
                     int64_t B, int64_t H, int64_t N, int64_t M, int d,
@@ -184,6 +198,21 @@ int attn_fwd_kv_outer(const void *q, const void *k, const void *v, void *o, floa
  * ATTN_ERR_HIP if the launch fails.  A row whose entries are all -inf gives NaN.
  */
 int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stream);
+
+/*
+ * online_softmax_lse -- online_softmax that also returns each row's
+ * log-sum-exp, LSE_r = m + log s = log sum_i e^{x[r,i]} (natural log), the
+ * normaliser's two numbers folded into one ("从原始Softmax到在线Softmax" page,
+ * "softmax形式推导": log-softmax = x - LSE).
+ *
+ * Arguments as online_softmax, plus
+ *   lse   [rows] float32 (device, written, 4-byte aligned), or NULL;
+ *   y     may be NULL: then only the LSE is computed, in one read of x
+ *         (pass 2 is skipped); y and lse must not both be NULL.
+ * Errors as online_softmax (ATTN_ERR_NULL when x is NULL or both outputs
+ * are).  A row whose entries are all -inf has LSE = -inf (and y NaN).
+ */
+int online_softmax_lse(const float *x, float *y, float *lse, int64_t rows, int64_t n, void *stream);
 
 /* Static, human-readable text for a return code (never NULL). */
 const char *attn_strerror(int code);

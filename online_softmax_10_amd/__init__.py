@@ -16,7 +16,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_splits", "fwd_kv_outer", "online_softmax", "softmax_xent", "plan", "lib", "AttnMask", "CAUSAL_MODES", "LIB_PATH", "AttnError",
+__all__ = ["fwd", "fwd_splits", "fwd_kv_outer", "online_softmax", "logsumexp", "softmax_xent", "plan", "lib", "AttnMask", "CAUSAL_MODES", "LIB_PATH", "AttnError",
            "ATTN_F32", "ATTN_BF16", "ATTN_MAX_SPLITS", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -28,7 +28,7 @@ ERROR_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATT
                -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_OVERFLOW", -7: "ATTN_ERR_HIP",
                -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_SPLITS", -10: "ATTN_ERR_MASK"}
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "attn_fwd_masked", "attn_fwd_kv_outer", "online_softmax",
-                    "softmax_xent", "attn_fwd_plan", "attn_strerror", "attn_last_error_detail")
+                    "online_softmax_lse", "softmax_xent", "attn_fwd_plan", "attn_strerror", "attn_last_error_detail")
 
 # attn_causal of include/attn.h, by the names fwd() accepts.
 CAUSAL_MODES = {False: 0, True: 1, "none": 0, "top_left": 1, "bottom_right": 2}
@@ -36,7 +36,9 @@ CAUSAL_MODES = {False: 0, True: 1, "none": 0, "top_left": 1, "bottom_right": 2}
 
 class AttnMask(ctypes.Structure):
     """struct attn_mask of include/attn.h."""
-    _fields_ = [("causal", ctypes.c_int), ("kv_len", ctypes.c_void_p)]
+    _fields_ = [("causal", ctypes.c_int), ("kv_len", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("bias_stride_b", ctypes.c_int64), ("bias_stride_h", ctypes.c_int64),
+                ("bias_stride_n", ctypes.c_int64)]
 
 _lib = None
 
@@ -74,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_kv_outer.restype = ctypes.c_int
         L.online_softmax.argtypes = [vp, vp, i64, i64, vp]
         L.online_softmax.restype = ctypes.c_int
+        L.online_softmax_lse.argtypes = [vp, vp, vp, i64, i64, vp]
+        L.online_softmax_lse.restype = ctypes.c_int
         L.attn_strerror.argtypes = [ctypes.c_int]
         L.attn_strerror.restype = ctypes.c_char_p
         L.attn_last_error_detail.argtypes = []
@@ -113,15 +117,45 @@ def _check_output(name, t, shape, dtype, device):
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
-def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None, kv_len=None):
+def _bias_operand(bias, B, H, N, M, device):
+    """A float32 bias broadcastable to [B,H,N,M] -> (tensor to pass, (sb, sh, sn)).
+
+    The library reads rows of M contiguous floats at 16-byte aligned addresses;
+    a bias that is not laid out so is copied into rows padded to a multiple of
+    4 elements (broadcast dimensions stay unexpanded).
+    """
+    import torch
+
+    if bias.dtype != torch.float32 or bias.device != device:
+        raise ValueError(f"bias must be a float32 tensor on {device}")
+    if bias.dim() > 4:
+        raise ValueError("bias must have at most 4 dimensions [B,H,N,M]")
+    try:
+        view = bias.expand(B, H, N, M)
+    except RuntimeError as e:
+        raise ValueError(f"bias of shape {tuple(bias.shape)} does not broadcast to {(B, H, N, M)}") from e
+    st = view.stride()
+    if st[3] != 1 or any(s % 4 for s in st[:3]) or view.data_ptr() % 16:
+        src = bias.reshape((1,) * (4 - bias.dim()) + tuple(bias.shape))
+        lead = src.shape[:3]
+        padded = torch.empty(lead + ((M + 3) // 4 * 4,), dtype=torch.float32, device=device)
+        padded[..., :M].copy_(src.expand(lead + (M,)))
+        view = padded[..., :M].expand(B, H, N, M)
+        st = view.stride()
+    return view, st[:3]
+
+
+def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None, kv_len=None, bias=None):
     """Attention forward with an explicit split count (0 = library's choice).
 
     q [B,H,N,d], k and v [B,H,M,d]: contiguous CUDA/HIP tensors of one dtype
     (bfloat16 or float32).  causal: False, True / "top_left" (key j masked for
     query i when j > i) or "bottom_right" (when j > i + M - N).  kv_len:
     optional contiguous int32 GPU tensor [B] of valid key counts (keys j >=
-    kv_len[b] masked).  Returns (o [B,H,N,d] same dtype, lse [B,H,N] float32);
-    a row with no visible key gets o = 0, lse = -inf.
+    kv_len[b] masked).  bias: optional float32 GPU tensor broadcastable to
+    [B,H,N,M], added to the scaled scores (-inf masks a key).  Returns
+    (o [B,H,N,d] same dtype, lse [B,H,N] float32); a row with no visible key
+    (or only -inf scores) gets o = 0, lse = -inf.
     """
     import torch
 
@@ -152,7 +186,7 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
     if causal not in CAUSAL_MODES:
         raise ValueError(f"causal must be one of {sorted(map(str, CAUSAL_MODES))}, got {causal!r}")
     mode = CAUSAL_MODES[causal]
-    if kv_len is None and mode != 2:
+    if kv_len is None and mode != 2 and bias is None:
         rc = lib().attn_fwd_splits(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                    B, H, N, M, d, float(scale), mode, code, int(num_splits),
                                    _stream_handle(q.device))
@@ -164,6 +198,9 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
                 or kv_len.numel() != B):
             raise ValueError(f"kv_len must be a contiguous int32 tensor of {B} entries on {q.device}")
     mask = AttnMask(mode, kv_len.data_ptr() if kv_len is not None else None)
+    if bias is not None:
+        bias, (sb, sh, sn) = _bias_operand(bias, B, H, N, M, q.device)
+        mask.bias, mask.bias_stride_b, mask.bias_stride_h, mask.bias_stride_n = bias.data_ptr(), sb, sh, sn
     rc = lib().attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                B, H, N, M, d, float(scale), ctypes.byref(mask), code, int(num_splits),
                                _stream_handle(q.device))
@@ -172,12 +209,13 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
     return out, lse
 
 
-def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None):
-    """softmax(mask(q k^T * scale)) v and the row log-sum-exp (natural log).
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None, bias=None):
+    """softmax(mask(q k^T * scale + bias)) v and the row log-sum-exp (natural log).
 
-    causal and kv_len as in fwd_splits.
+    causal, kv_len and bias as in fwd_splits.
     """
-    return fwd_splits(q, k, v, scale=scale, causal=causal, num_splits=0, out=out, lse=lse, kv_len=kv_len)
+    return fwd_splits(q, k, v, scale=scale, causal=causal, num_splits=0, out=out, lse=lse, kv_len=kv_len,
+                      bias=bias)
 
 
 def fwd_kv_outer(q, k, v, scale=None, causal=False, out=None, lse=None):
@@ -230,8 +268,12 @@ def plan(B, H, N, M, d, dtype="bf16", num_splits=0):
     return name.decode(), splits.value
 
 
-def online_softmax(x, out=None):
-    """Row-wise softmax of a contiguous float32 GPU tensor over its last axis."""
+def online_softmax(x, out=None, return_lse=False, lse=None):
+    """Row-wise softmax of a contiguous float32 GPU tensor over its last axis.
+
+    return_lse: also return the rows' log-sum-exp (float32, x.shape[:-1]),
+    i.e. (y, lse).
+    """
     import torch
 
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
@@ -242,9 +284,41 @@ def online_softmax(x, out=None):
         out = torch.empty_like(x)
     else:
         _check_output("out", out, tuple(x.shape), torch.float32, x.device)
-    rc = lib().online_softmax(x.data_ptr(), out.data_ptr(), rows, n, _stream_handle(x.device))
+    if not return_lse:
+        rc = lib().online_softmax(x.data_ptr(), out.data_ptr(), rows, n, _stream_handle(x.device))
+        if rc != 0:
+            raise AttnError(rc, "online_softmax")
+        return out
+    lse = _lse_output(x, lse)
+    rc = lib().online_softmax_lse(x.data_ptr(), out.data_ptr(), lse.data_ptr(), rows, n, _stream_handle(x.device))
     if rc != 0:
-        raise AttnError(rc, "online_softmax")
+        raise AttnError(rc, "online_softmax_lse")
+    return out, lse
+
+
+def _lse_output(x, lse):
+    import torch
+
+    shape = tuple(x.shape[:-1]) if x.dim() > 0 else ()
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check_output("lse", lse, shape, torch.float32, x.device)
+    return lse
+
+
+def logsumexp(x, out=None):
+    """log sum exp over the last axis of a contiguous float32 GPU tensor: the
+    normaliser of online_softmax alone, one read of x."""
+    import torch
+
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    n = x.shape[-1] if x.dim() > 0 else 1
+    rows = x.numel() // n if n > 0 else 0
+    out = _lse_output(x, out)
+    rc = lib().online_softmax_lse(x.data_ptr(), None, out.data_ptr(), rows, n, _stream_handle(x.device))
+    if rc != 0:
+        raise AttnError(rc, "online_softmax_lse")
     return out
 
 

@@ -34,8 +34,9 @@ struct Plan {
 };
 
 // Work decomposition.  num_splits: 0 = choose, 1 = single pass, >= 2 = split.
-Plan plan_for(int64_t BH, int64_t N, int64_t M, bool bf16, int num_splits) {
-    const bool few_queries = N <= osa::kDecodeMaxQueries;
+// Calls with a bias never take the decode kernel.
+Plan plan_for(int64_t BH, int64_t N, int64_t M, bool bf16, int num_splits, bool bias = false) {
+    const bool few_queries = N <= osa::kDecodeMaxQueries && !bias;
     if (num_splits == 1) return Plan{Plan::SINGLE, 1, 0};
     if (few_queries) {
         // Decode shape: stream K/V with enough workgroups in flight; each split
@@ -76,6 +77,11 @@ int validate_attn(const void *q, const void *k, const void *v, const void *o, co
     if (B < 0 || H < 0 || N < 0 || M < 0) return ATTN_ERR_SHAPE;
     if (mask && (mask->causal < ATTN_CAUSAL_NONE || mask->causal > ATTN_CAUSAL_BOTTOM_RIGHT)) return ATTN_ERR_MASK;
     if (mask && mask->kv_len && (reinterpret_cast<uintptr_t>(mask->kv_len) & 3u)) return ATTN_ERR_ALIGN;
+    if (mask && mask->bias) {
+        if (mask->bias_stride_b < 0 || mask->bias_stride_h < 0 || mask->bias_stride_n < 0) return ATTN_ERR_SHAPE;
+        if (!aligned16(mask->bias) || ((mask->bias_stride_b | mask->bias_stride_h | mask->bias_stride_n) & 3))
+            return ATTN_ERR_ALIGN;
+    }
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
     if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
@@ -92,11 +98,12 @@ int validate_attn(const void *q, const void *k, const void *v, const void *o, co
 
 // The kernel that carries the attention itself for a plan (the split paths
 // add the merge kernel).
-enum class MainKernel { F32, BF16_4W, BF16_8W, DECODE };
+enum class MainKernel { F32, BF16_4W, BF16_8W, DECODE, BF16_BIAS };
 
-MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16) {
+MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16, bool bias = false) {
     if (plan.kind == Plan::DECODE) return MainKernel::DECODE;
     if (!bf16) return MainKernel::F32;
+    if (bias) return MainKernel::BF16_BIAS;
     // The eight-wave kernel shares each K/V tile among 256 rows; use it for
     // single-pass problems whose 256-row tiles alone give every compute unit
     // a workgroup.
@@ -110,6 +117,7 @@ const char *main_kernel_name(MainKernel k) {
     case MainKernel::BF16_4W: return "attn_fwd_bf16_kernel";
     case MainKernel::BF16_8W: return "attn_fwd_bf16_w8_kernel";
     case MainKernel::DECODE: return "attn_decode_kernel";
+    case MainKernel::BF16_BIAS: return "attn_fwd_bf16_bias_kernel";
     }
     return "";
 }
@@ -135,6 +143,12 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     p.H = (int)H;
     const int causal = mask ? mask->causal : ATTN_CAUSAL_NONE;
     p.kv_len = mask ? mask->kv_len : nullptr;
+    p.bias = mask ? mask->bias : nullptr;
+    if (p.bias) {
+        p.bias_sb = mask->bias_stride_b;
+        p.bias_sh = mask->bias_stride_h;
+        p.bias_sn = mask->bias_stride_n;
+    }
     p.causal_off = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? (int)(M - N) : 0;
     // Scores are kept in base-2 units.  c is at least the smallest normal float
     // so that a masked score (-inf) times c is -inf, never NaN; for scale = 0
@@ -143,10 +157,10 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     p.negate_q = signbit(scale) != 0;
     p.causal = causal != ATTN_CAUSAL_NONE;
 
-    const Plan plan = plan_for(BH, N, M, bf16, num_splits);
+    const Plan plan = plan_for(BH, N, M, bf16, num_splits, p.bias != nullptr);
     const int64_t blocks = plan.kind == Plan::DECODE ? BH * plan.splits : BH * ceil_div(N, 128) * plan.splits;
     if (blocks > kMaxBlocks) return ATTN_ERR_OVERFLOW;
-    const MainKernel kernel = main_kernel(plan, BH, N, bf16);
+    const MainKernel kernel = main_kernel(plan, BH, N, bf16, p.bias != nullptr);
     p.splits = plan.splits;
     p.tiles_per_split = plan.tiles_per_split;
     if (plan.kind == Plan::SINGLE) {
@@ -176,7 +190,7 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     if (kernel == MainKernel::DECODE)
         e = osa::launch_attn_decode(p, bf16, stream);
     else
-        e = kernel == MainKernel::BF16_4W ? osa::launch_attn_bf16(p, stream) : osa::launch_attn_f32(p, stream);
+        e = kernel == MainKernel::F32 ? osa::launch_attn_f32(p, stream) : osa::launch_attn_bf16(p, stream);
     if (e == hipSuccess) {
         e = osa::launch_split_merge(p, bf16, stream);
         if (e != hipSuccess) set_detail("split merge kernel launch", e);
@@ -258,19 +272,25 @@ int attn_fwd_kv_outer(const void *q, const void *k, const void *v, void *o, floa
     return ATTN_OK;
 }
 
-int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stream) {
+int online_softmax_lse(const float *x, float *y, float *lse, int64_t rows, int64_t n, void *stream) {
     if (rows < 0 || n < 0) return ATTN_ERR_SHAPE;
     if (rows == 0) return ATTN_OK;
     if (n < 1) return ATTN_ERR_SHAPE;
-    if (!x || !y) return ATTN_ERR_NULL;
-    if (!aligned16(x) || !aligned16(y)) return ATTN_ERR_ALIGN;
+    if (!x || (!y && !lse)) return ATTN_ERR_NULL;
+    if (!aligned16(x) || (y && !aligned16(y)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return ATTN_ERR_ALIGN;
     if (n > kI32Max || rows > (int64_t(1) << 62) / n) return ATTN_ERR_OVERFLOW;
-    const hipError_t e = osa::launch_online_softmax(x, y, rows, n, static_cast<hipStream_t>(stream));
+    const hipError_t e = osa::launch_online_softmax(x, y, lse, rows, n, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         set_detail("online softmax kernel launch", e);
         return ATTN_ERR_HIP;
     }
     return ATTN_OK;
+}
+
+int online_softmax(const float *x, float *y, int64_t rows, int64_t n, void *stream) {
+    if (rows > 0 && n > 0 && !y) return ATTN_ERR_NULL;
+    return online_softmax_lse(x, y, nullptr, rows, n, stream);
 }
 
 int softmax_xent(const float *x, const int64_t *labels, float *loss, float *lse, float *mean, int64_t rows,

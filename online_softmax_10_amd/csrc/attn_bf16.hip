@@ -47,13 +47,15 @@ using namespace bf16;
 // Nothing is scheduled across this point.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-template <int NW, int D, bool CAUSAL, bool SPLIT>
+template <int NW, int D, bool CAUSAL, bool SPLIT, bool BIAS>
 __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                           const uint16_t *__restrict__ v, uint16_t *__restrict__ o,
                                           float *__restrict__ lse, float *__restrict__ part_o,
                                           float *__restrict__ part_lse, int BH, int N, int M, float c,
                                           uint32_t qsign, int ntq, int splits, int tiles_per_split,
-                                          const int32_t *__restrict__ kv_len, int H, int coff) {
+                                          const int32_t *__restrict__ kv_len, int H, int coff,
+                                          const float *__restrict__ bias, int64_t bias_sb, int64_t bias_sh,
+                                          int64_t bias_sn) {
     using T = Tile<D>;
     constexpr int BR = 32 * NW;           // query rows per workgroup
     constexpr int LOADS = T::LOADS / NW;  // LDS-direct loads per wave per tile, for K and for V
@@ -90,8 +92,15 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     const u32x4 krs = make_rsrc(k + (size_t)bh * M * D, (uint32_t)M * T::RB);
     const u32x4 vrs = make_rsrc(v + (size_t)bh * M * D, (uint32_t)M * T::RB);
 
+    // With a bias the scores are brought to base-2 units (bias included)
+    // before the tile math, which then runs with c = 1.
     WaveTile<D, CAUSAL> wt;
-    wt.init(q + (size_t)bh * N * D, N, q0 + wave * 32, lane, c, qsign, coff);
+    wt.init(q + (size_t)bh * N * D, N, q0 + wave * 32, lane, BIAS ? 1.f : c, qsign, coff);
+    const float *brow = nullptr;  // this lane's bias row (rows past N read row N - 1)
+    f32x4 bnext[8];               // bias of the next tile this wave computes
+    if constexpr (BIAS)
+        brow = bias + (int64_t)(bh / H) * bias_sb + (int64_t)(bh % H) * bias_sh +
+               (int64_t)min(wt.qrow, N - 1) * bias_sn;
 
     int ld_off[LOADS];
 #pragma unroll
@@ -114,6 +123,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         constexpr bool FULL = decltype(full)::value;
         constexpr bool LOADS_ON = decltype(loads)::value;
         wait_loads_and_barrier<0>();
+        if constexpr (BIAS) wt.apply_bias(bnext, s_cur, c);  // tile j's bias landed with the wait above
         wt.mask(kb + j * BC, ke, s_cur);
         const float m = wt.m_run;
         uint32_t popw[BC / 16][4];
@@ -156,6 +166,9 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         float alpha = 1.f;
         if (__builtin_amdgcn_ballot_w64(!(lsum <= SHIFT_SUM_LIMIT)) != 0) alpha = wt.exact_shift(s_cur, pop, lsum);
         wt.l_run = alpha * wt.l_run + lsum;
+        // Tile j+1's bias, over the P.V phase (its registers are free once the
+        // scores of tile j are packed into pop).
+        if constexpr (BIAS && FULL) wt.bias_fetch(brow, kb + (j + 1) * BC, M, bnext);
 
         bf16x8 vop[3];
         vop[0] = wt.vread(vs_cur, 0);
@@ -196,6 +209,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             load(krs, 0, lds_k0, i);
             load(vrs, 0, lds_v0, i);
         }
+        if constexpr (BIAS) wt.bias_fetch(brow, kb, M, bnext);
         wait_loads_and_barrier<0>();
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) load(krs, min(1, ntiles - 1), lds_k1, i);
@@ -253,26 +267,42 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(ATTN_KERNEL_ARGS) {
-    attn_body<4, D, CAUSAL, SPLIT>(ATTN_KERNEL_PASS);
+    attn_body<4, D, CAUSAL, SPLIT, false>(ATTN_KERNEL_PASS, nullptr, 0, 0, 0);
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_w8_kernel(ATTN_KERNEL_ARGS) {
-    attn_body<8, D, CAUSAL, SPLIT>(ATTN_KERNEL_PASS);
+    attn_body<8, D, CAUSAL, SPLIT, false>(ATTN_KERNEL_PASS, nullptr, 0, 0, 0);
+}
+
+// The four-wave kernel with an additive score bias.  The bias prefetch takes
+// 32 more registers per lane: at d = 128 that exceeds the 256 of two
+// workgroups per CU, so there the kernel runs one workgroup per CU.
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_fwd_bf16_bias_kernel(ATTN_KERNEL_ARGS, const float *__restrict__ bias,
+                                                                    int64_t bias_sb, int64_t bias_sh,
+                                                                    int64_t bias_sn) {
+    attn_body<4, D, CAUSAL, SPLIT, true>(ATTN_KERNEL_PASS, bias, bias_sb, bias_sh, bias_sn);
 }
 
 template <int NW, int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
     const int rows = 32 * NW;
     const int ntq = (p.N + rows - 1) / rows;
-    const int64_t blocks = (int64_t)p.BH * ntq * p.splits;
+    const dim3 grid((unsigned)((int64_t)p.BH * ntq * p.splits));
     const uint32_t qsign = p.negate_q ? 0x80008000u : 0u;
-    auto kernel = NW == 8 ? attn_fwd_bf16_w8_kernel<D, CAUSAL, SPLIT> : attn_fwd_bf16_kernel<D, CAUSAL, SPLIT>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * NW), 0, stream,
-                       static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
-                       static_cast<const uint16_t *>(p.v), static_cast<uint16_t *>(p.o), p.lse, p.part_o,
-                       p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split, p.kv_len, p.H,
-                       p.causal_off);
+    const uint16_t *q = static_cast<const uint16_t *>(p.q), *k = static_cast<const uint16_t *>(p.k),
+                   *v = static_cast<const uint16_t *>(p.v);
+    uint16_t *o = static_cast<uint16_t *>(p.o);
+    if (NW == 4 && p.bias != nullptr) {
+        hipLaunchKernelGGL((attn_fwd_bf16_bias_kernel<D, CAUSAL, SPLIT>), grid, dim3(256), 0, stream, q, k, v, o,
+                           p.lse, p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits,
+                           p.tiles_per_split, p.kv_len, p.H, p.causal_off, p.bias, p.bias_sb, p.bias_sh, p.bias_sn);
+    } else {
+        auto kernel = NW == 8 ? attn_fwd_bf16_w8_kernel<D, CAUSAL, SPLIT> : attn_fwd_bf16_kernel<D, CAUSAL, SPLIT>;
+        hipLaunchKernelGGL(kernel, grid, dim3(64 * NW), 0, stream, q, k, v, o, p.lse, p.part_o, p.part_lse, p.BH,
+                           p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split, p.kv_len, p.H, p.causal_off);
+    }
     return hipGetLastError();
 }
 
@@ -286,11 +316,12 @@ hipError_t launch_d(const AttnProblem &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream) {
+    // Also the kernel for calls with a bias.
     return p.d == 64 ? launch_d<4, 64>(p, stream) : launch_d<4, 128>(p, stream);
 }
 
 hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream) {
-    // Single pass only (the front end never asks this kernel for partials).
+    // Single pass, no bias (the front end never asks this kernel for either).
     return p.d == 64 ? launch_d<8, 64>(p, stream) : launch_d<8, 128>(p, stream);
 }
 

@@ -55,6 +55,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int BC = kBf16KeyTile;  // keys per tile
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994531f;
+constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SHIFT_SUM_LIMIT = 65536.f;  // 2^16: largest tile sum kept against a stale shift
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data
 
@@ -214,6 +215,37 @@ struct WaveTile {
                     s[cb][r] = ok ? s[cb][r] : NEG_INF;
                 }
         }
+    }
+
+    // Additive bias: the 32 bias values of this lane's scores of the tile at
+    // kv0 (register r of block cb is key kv0 + 32*cb + 16*(r/8) + 8*hh + r%8:
+    // two runs of four), from the bias row of its query.  Keys at or past M
+    // read as 0 (they are masked).
+    __device__ __forceinline__ void bias_fetch(const float *brow, int kv0, int M, f32x4 (&b)[8]) const {
+#pragma unroll
+        for (int run = 0; run < 8; ++run) {
+            const int key = kv0 + 32 * (run >> 2) + 16 * ((run >> 1) & 1) + 8 * hh + 4 * (run & 1);
+            if (key + 4 <= M) {
+                b[run] = *reinterpret_cast<const f32x4 *>(brow + key);
+            } else {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = key + e < M ? brow[key + e] : 0.f;
+                b[run] = x;
+            }
+        }
+    }
+
+    // s <- c_scale * s + log2(e) * bias: scores in base-2 units with the bias
+    // added (the tile math then runs with c = 1).
+    __device__ __forceinline__ void apply_bias(const f32x4 (&b)[8], f32x16 (&s)[2], float c_scale) const {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int run = 4 * cb + 2 * (r >> 3) + ((r & 7) >> 2);
+                s[cb][r] = __builtin_fmaf(s[cb][r], c_scale, b[run][r & 3] * LOG2E);
+            }
     }
 
     // P = 2^(c*s - m) for shift m, rounded to bf16 as the operands of P.V;

@@ -31,6 +31,7 @@ constexpr int BR = 32 * NW;
 constexpr int BC = kF32KeyTile;  // 32 keys per tile
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994531f;
+constexpr float LOG2E = 1.4426950408889634f;
 
 template <int D>
 struct Layout {
@@ -54,7 +55,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     float *__restrict__ o, float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
     int BH, int N, int M, float c, float qsign, int ntq, int splits, int tiles_per_split,
-    const int32_t *__restrict__ kv_len, int H, int coff) {
+    const int32_t *__restrict__ kv_len, int H, int coff, const float *__restrict__ bias, int64_t bias_sb,
+    int64_t bias_sh, int64_t bias_sn) {
     using Lay = Layout<D>;
     __shared__ __attribute__((aligned(16))) float Ks[BC * Lay::KS];
     __shared__ __attribute__((aligned(16))) float Vs[BC * Lay::VS];
@@ -79,6 +81,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
     if (kv_len != nullptr) ke = min(ke, max(kv_len[bh / H], 0));
     if (CAUSAL) ke = min(ke, q0 + BR + coff);
     const int ntiles = ke > kb ? (ke - kb + BC - 1) / BC : 0;
+
+    // Additive bias: this lane's row (rows past N read row N - 1).  With a
+    // bias the scores are brought to base-2 units (bias included) right after
+    // the product and the rest runs with cs = 1.
+    const bool has_bias = bias != nullptr;
+    const float *brow = has_bias ? bias + (int64_t)(bh / H) * bias_sb + (int64_t)(bh % H) * bias_sh +
+                                       (int64_t)min(qrow, N - 1) * bias_sn
+                                 : nullptr;
+    const float cs = has_bias ? 1.f : c;
 
     const float *qh = q + (size_t)bh * N * D;
     const float *kh = k + (size_t)bh * M * D;
@@ -131,11 +142,30 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
         if (t + 1 < ntiles) fetch(kv0 + BC);
         if (CAUSAL && kv0 > wq_lo + 31 + coff) continue;
 
+        // Bias of this lane's scores (register r: key kv0 + 8*(r/4) + 4*hh + r%4),
+        // fetched before the product so the loads overlap it; keys past M read 0.
+        f32x4 bv[4];
+        if (has_bias) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int key = kv0 + 8 * g + 4 * hh;
+                if (key + 4 <= M) {
+                    bv[g] = *reinterpret_cast<const f32x4 *>(brow + key);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bv[g][e] = key + e < M ? brow[key + e] : 0.f;
+                }
+            }
+        }
         f32x16 s = f32x16{};
         const float *krow = &Ks[l32 * Lay::KS + hh];
 #pragma unroll
         for (int kk = 0; kk < D / 2; ++kk)
             s = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * kk], qop[kk], s, 0, 0, 0);
+        if (has_bias) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(s[r], c, bv[r >> 2][r & 3] * LOG2E);
+        }
 
         // Register r holds key kv0 + 8*(r/4) + 4*hh + r%4.
         const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > wq_lo + coff);
@@ -151,7 +181,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
         mx = xhalf_max(mx);
-        const float m_tile = mx == NEG_INF ? NEG_INF : mx * c;
+        const float m_tile = mx == NEG_INF ? NEG_INF : mx * cs;
         const float m_new = fmaxf(m_run, m_tile);
         const float m_use = m_new == NEG_INF ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -160,7 +190,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
         float lsum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m_use));
+            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], cs, -m_use));
             if (need_mask) e = s[r] == NEG_INF ? 0.f : e;
             s[r] = e;
             lsum += e;
@@ -212,7 +242,7 @@ hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
                        static_cast<const float *>(p.q), static_cast<const float *>(p.k),
                        static_cast<const float *>(p.v), static_cast<float *>(p.o), p.lse, p.part_o, p.part_lse,
                        p.BH, p.N, p.M, p.c, p.negate_q ? -1.f : 1.f, ntq, p.splits, p.tiles_per_split, p.kv_len,
-                       p.H, p.causal_off);
+                       p.H, p.causal_off, p.bias, p.bias_sb, p.bias_sh, p.bias_sn);
     return hipGetLastError();
 }
 

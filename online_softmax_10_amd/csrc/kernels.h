@@ -15,6 +15,10 @@ struct AttnProblem {
     int BH, N, M, d;
     int H;                   // heads per batch (batch of head bh = bh / H)
     const int32_t *kv_len;   // [B] valid keys per batch (device; clamped to [0, M]), or nullptr
+    // Additive score bias, fp32, or nullptr: element (b, h, i, j) at
+    // bias[b*bias_sb + h*bias_sh + i*bias_sn + j]; 16-byte aligned rows.
+    const float *bias;
+    int64_t bias_sb, bias_sh, bias_sn;
     int causal_off;          // causal: key j visible for query i iff j <= i + causal_off
     float c;                 // |scale| * log2(e): scores are kept in base-2 units
     bool negate_q;           // scale < 0: q's sign is flipped on load so c >= 0
@@ -49,7 +53,8 @@ hipError_t launch_split_merge(const AttnProblem &p, bool bf16, hipStream_t strea
 // fp32 workspace ws_o [BH,N,d], ws_m, ws_l [BH,N]); bf16, single pass, no mask
 // beyond top-left causal.
 hipError_t launch_attn_kv_outer(const AttnProblem &p, float *ws_o, float *ws_m, float *ws_l, hipStream_t stream);
-hipError_t launch_online_softmax(const float *x, float *y, int64_t rows, int64_t n, hipStream_t stream);
+// y and lse may each be nullptr (not both): softmax rows, row LSE, or both.
+hipError_t launch_online_softmax(const float *x, float *y, float *lse, int64_t rows, int64_t n, hipStream_t stream);
 // loss[i] = LSE_i - x[i, labels[i]] (NaN for a label outside [0, n)); lse and
 // mean optional (nullptr): the row LSE and the mean of the losses.
 hipError_t launch_softmax_xent(const float *x, const int64_t *labels, float *loss, float *lse, float *mean,

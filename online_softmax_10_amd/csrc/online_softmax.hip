@@ -4,7 +4,9 @@
 // elements it visits (m_i = max(m_{i-1}, x_i), s_i = s_{i-1} e^{m_{i-1}-m_i}
 // + e^{x_i - m_i}), a chunk of four elements at a time; the 64 lane states are
 // merged with the same rule (max of the two maxima, each sum rescaled to it).
-// Pass 2 writes y = e^{x - m} / s.  Two reads and one write per element,
+// Pass 2 writes y = e^{x - m} / s.  Optionally the row's log-sum-exp
+// LSE = m + log s goes out too, and with y absent pass 2 is skipped (one read
+// per element: the log-sum-exp reduction alone).  Two reads and one write per element,
 // against three reads and one write for the three-pass safe softmax.  Rows
 // whose length is a multiple of 4 and at most 65536 stay in registers between
 // the passes, so they are read once: up to 4096 elements in one wave, longer
@@ -62,9 +64,13 @@ __device__ __forceinline__ MS merge(MS a, MS b) {
     return MS{m, sa + sb};
 }
 
+// Lane 0 writes the row's LSE = m + log s (natural log) when asked.
+__device__ __forceinline__ void write_lse(float *lse_r, MS st, int lane) {
+    if (lse_r != nullptr && lane == 0) *lse_r = st.m + logf(st.s);
+}
+
 template <bool VEC>
-__device__ __forceinline__ void softmax_row(const float *xr, float *yr, int64_t n,
-                                            int lane) {
+__device__ __forceinline__ void softmax_row(const float *xr, float *yr, float *lse_r, int64_t n, int lane) {
     MS st{NEG_INF, 0.f};
     if constexpr (VEC) {
         const int64_t nv = n >> 2;
@@ -84,6 +90,8 @@ __device__ __forceinline__ void softmax_row(const float *xr, float *yr, int64_t 
         MS o{__shfl_xor(st.m, off, 64), __shfl_xor(st.s, off, 64)};
         st = merge(st, o);
     }
+    write_lse(lse_r, st, lane);
+    if (yr == nullptr) return;
     const float m = st.m;
     const float inv = 1.f / st.s;
     if constexpr (VEC) {
@@ -103,7 +111,7 @@ __device__ __forceinline__ void softmax_row(const float *xr, float *yr, int64_t 
 // Rows of n <= 256*R elements (n % 4 == 0) held in registers: each lane keeps
 // R float4 chunks (chunk i + 64 r of the row), so the row is read once.
 template <int R>
-__device__ __forceinline__ void softmax_row_regs(const float *xr, float *yr, int64_t n, int lane) {
+__device__ __forceinline__ void softmax_row_regs(const float *xr, float *yr, float *lse_r, int64_t n, int lane) {
     const int64_t nv = n >> 2;
     f32x4 v[R];
 #pragma unroll
@@ -123,6 +131,8 @@ __device__ __forceinline__ void softmax_row_regs(const float *xr, float *yr, int
         MS o{__shfl_xor(st.m, off, 64), __shfl_xor(st.s, off, 64)};
         st = merge(st, o);
     }
+    write_lse(lse_r, st, lane);
+    if (yr == nullptr) return;
     const float m = st.m;
     const float inv = 1.f / st.s;
 #pragma unroll
@@ -138,24 +148,25 @@ __device__ __forceinline__ void softmax_row_regs(const float *xr, float *yr, int
 }
 
 template <int R>
-__global__ __launch_bounds__(256) void online_softmax_regs_kernel(const float *x, float *y, int64_t rows, int64_t n) {
+__global__ __launch_bounds__(256) void online_softmax_regs_kernel(const float *x, float *y, float *lse, int64_t rows,
+                                                                  int64_t n) {
     const int lane = threadIdx.x & 63;
     for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4)
-        softmax_row_regs<R>(x + row * n, y + row * n, n, lane);
+        softmax_row_regs<R>(x + row * n, y ? y + row * n : nullptr, lse ? lse + row : nullptr, n, lane);
 }
 
 // Rows of 4096 < n <= 1024*4*R elements (n % 4 == 0): one 1024-thread
 // workgroup per row, R float4 chunks per thread (chunk t + 1024 r), wave
 // states merged through LDS.
 template <int R>
-__global__ __launch_bounds__(1024) void online_softmax_wide_kernel(const float *x, float *y, int64_t rows,
+__global__ __launch_bounds__(1024) void online_softmax_wide_kernel(const float *x, float *y, float *lse, int64_t rows,
                                                                    int64_t n) {
     __shared__ MS part[16];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t nv = n >> 2;
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
         const f32x4 *xr = reinterpret_cast<const f32x4 *>(x + row * n);
-        f32x4 *yr = reinterpret_cast<f32x4 *>(y + row * n);
+        f32x4 *yr = y ? reinterpret_cast<f32x4 *>(y + row * n) : nullptr;
         f32x4 v[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -179,6 +190,8 @@ __global__ __launch_bounds__(1024) void online_softmax_wide_kernel(const float *
 #pragma unroll
         for (int w = 1; w < 16; ++w) all = merge(all, part[w]);
         __syncthreads();  // part[] is rewritten by the next row
+        write_lse(lse ? lse + row : nullptr, all, t);
+        if (yr == nullptr) continue;
         const float m = all.m;
         const float inv = 1.f / all.s;
 #pragma unroll
@@ -196,44 +209,44 @@ __global__ __launch_bounds__(1024) void online_softmax_wide_kernel(const float *
 
 // Grid-stride over rows, one wave per row.
 template <bool VEC>
-__global__ __launch_bounds__(256) void online_softmax_kernel(const float *x, float *y,
-                                                             int64_t rows, int64_t n) {
+__global__ __launch_bounds__(256) void online_softmax_kernel(const float *x, float *y, float *lse, int64_t rows,
+                                                             int64_t n) {
     const int lane = threadIdx.x & 63;
     for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4)
-        softmax_row<VEC>(x + row * n, y + row * n, n, lane);
+        softmax_row<VEC>(x + row * n, y ? y + row * n : nullptr, lse ? lse + row : nullptr, n, lane);
 }
 
 }  // namespace
 
-hipError_t launch_online_softmax(const float *x, float *y, int64_t rows, int64_t n, hipStream_t stream) {
+hipError_t launch_online_softmax(const float *x, float *y, float *lse, int64_t rows, int64_t n, hipStream_t stream) {
     const int64_t want = (rows + 3) / 4;
     const dim3 grid((unsigned)(want < 65536 ? want : 65536));
     if ((n & 3) == 0 && n <= 4096) {
         // Smallest power-of-two chunk count per lane that holds the row.
         if (n <= 256)
-            hipLaunchKernelGGL((online_softmax_regs_kernel<1>), grid, dim3(256), 0, stream, x, y, rows, n);
+            hipLaunchKernelGGL((online_softmax_regs_kernel<1>), grid, dim3(256), 0, stream, x, y, lse, rows, n);
         else if (n <= 512)
-            hipLaunchKernelGGL((online_softmax_regs_kernel<2>), grid, dim3(256), 0, stream, x, y, rows, n);
+            hipLaunchKernelGGL((online_softmax_regs_kernel<2>), grid, dim3(256), 0, stream, x, y, lse, rows, n);
         else if (n <= 1024)
-            hipLaunchKernelGGL((online_softmax_regs_kernel<4>), grid, dim3(256), 0, stream, x, y, rows, n);
+            hipLaunchKernelGGL((online_softmax_regs_kernel<4>), grid, dim3(256), 0, stream, x, y, lse, rows, n);
         else if (n <= 2048)
-            hipLaunchKernelGGL((online_softmax_regs_kernel<8>), grid, dim3(256), 0, stream, x, y, rows, n);
+            hipLaunchKernelGGL((online_softmax_regs_kernel<8>), grid, dim3(256), 0, stream, x, y, lse, rows, n);
         else
-            hipLaunchKernelGGL((online_softmax_regs_kernel<16>), grid, dim3(256), 0, stream, x, y, rows, n);
+            hipLaunchKernelGGL((online_softmax_regs_kernel<16>), grid, dim3(256), 0, stream, x, y, lse, rows, n);
     } else if ((n & 3) == 0 && n <= 65536) {
         const dim3 wgrid((unsigned)(rows < 65536 ? rows : 65536));
         if (n <= 8192)
-            hipLaunchKernelGGL((online_softmax_wide_kernel<2>), wgrid, dim3(1024), 0, stream, x, y, rows, n);
+            hipLaunchKernelGGL((online_softmax_wide_kernel<2>), wgrid, dim3(1024), 0, stream, x, y, lse, rows, n);
         else if (n <= 16384)
-            hipLaunchKernelGGL((online_softmax_wide_kernel<4>), wgrid, dim3(1024), 0, stream, x, y, rows, n);
+            hipLaunchKernelGGL((online_softmax_wide_kernel<4>), wgrid, dim3(1024), 0, stream, x, y, lse, rows, n);
         else if (n <= 32768)
-            hipLaunchKernelGGL((online_softmax_wide_kernel<8>), wgrid, dim3(1024), 0, stream, x, y, rows, n);
+            hipLaunchKernelGGL((online_softmax_wide_kernel<8>), wgrid, dim3(1024), 0, stream, x, y, lse, rows, n);
         else
-            hipLaunchKernelGGL((online_softmax_wide_kernel<16>), wgrid, dim3(1024), 0, stream, x, y, rows, n);
+            hipLaunchKernelGGL((online_softmax_wide_kernel<16>), wgrid, dim3(1024), 0, stream, x, y, lse, rows, n);
     } else if ((n & 3) == 0)
-        hipLaunchKernelGGL((online_softmax_kernel<true>), grid, dim3(256), 0, stream, x, y, rows, n);
+        hipLaunchKernelGGL((online_softmax_kernel<true>), grid, dim3(256), 0, stream, x, y, lse, rows, n);
     else
-        hipLaunchKernelGGL((online_softmax_kernel<false>), grid, dim3(256), 0, stream, x, y, rows, n);
+        hipLaunchKernelGGL((online_softmax_kernel<false>), grid, dim3(256), 0, stream, x, y, lse, rows, n);
     return hipGetLastError();
 }
 

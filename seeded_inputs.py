@@ -122,6 +122,29 @@ def make_rows(rows: int, n: int, seed: int, dist: str = "normal", spread: float 
     return (x * np.float32(spread)).astype(np.float32)
 
 
+def make_bias(shape, seed: int, kind: str = "normal", neg_inf_frac: float = 0.0) -> np.ndarray:
+    """float32 additive score bias of `shape` (broadcastable to [B,H,N,M]).
+
+    "normal": N(0, 2^2) entries.  "distance": -slope_h * |i - j| with slopes
+    2^(-8 (h+1) / H) over the head axis (a position-distance penalty; the
+    shape must be [1,H,N,M]).  neg_inf_frac: that fraction of entries, drawn
+    at random, set to -inf (masked keys).
+    """
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        b = rng.standard_normal(shape, dtype=np.float32) * np.float32(2.0)
+    elif kind == "distance":
+        _, H, N, M = shape
+        slope = np.exp2(-8.0 * (np.arange(H) + 1) / H).reshape(1, H, 1, 1)
+        dist = np.abs(np.arange(N).reshape(1, 1, N, 1) - np.arange(M).reshape(1, 1, 1, M))
+        b = (-slope * dist).astype(np.float32)
+    else:
+        raise ValueError(f"unknown bias kind {kind!r}")
+    if neg_inf_frac > 0:
+        b = np.where(rng.random(b.shape) < neg_inf_frac, np.float32(-np.inf), b).astype(np.float32)
+    return np.ascontiguousarray(b)
+
+
 def sample_rows(w: Workload, count: int, seed: int = 1234) -> np.ndarray:
     """Flat row indices r = (b*H + h)*N + i to sample at full size.
 

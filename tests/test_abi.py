@@ -120,6 +120,18 @@ def test_online_softmax_validation(L, buf):
     assert f(None, None, 0, 0, None) == OK
 
 
+def test_online_softmax_lse_validation(L, buf):
+    f = L.online_softmax_lse
+    assert f(buf, buf, buf, -1, 3, None) == SHAPE
+    assert f(buf, buf, buf, 2, 0, None) == SHAPE
+    assert f(buf, None, None, 1, 3, None) == NULL   # no output at all
+    assert f(None, buf, buf, 1, 3, None) == NULL
+    assert f(buf, buf, buf + 2, 1, 3, None) == ALIGN  # lse needs 4-byte alignment
+    assert f(buf, buf + 8, buf, 1, 3, None) == ALIGN
+    assert f(buf, None, buf, 1, 2**31, None) == OVERFLOW
+    assert f(None, None, None, 0, 5, None) == OK
+
+
 def test_binding_raises_without_gpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(2, 3)
@@ -178,6 +190,16 @@ def test_softmax_xent_validation(L, buf):
     assert f(buf, buf, buf, None, None, 2**40, 2**30, None) == OVERFLOW
     assert f(None, None, None, None, None, 0, 5, None) == OK
     assert f(None, None, None, None, None, 0, 0, None) == OK
+
+
+def test_bias_validation(L, buf):
+    f = L.attn_fwd_masked
+    args = lambda mask: (buf, buf, buf, buf, buf, 1, 1, 4, 4, 64, 0.125, ctypes.byref(mask), 1, 0, None)
+    assert f(*args(osa.AttnMask(0, None, buf + 4, 0, 0, 4))) == ALIGN  # bias pointer not 16-byte aligned
+    assert f(*args(osa.AttnMask(0, None, buf, 0, 0, 6))) == ALIGN      # row stride not a multiple of 4
+    assert f(*args(osa.AttnMask(0, None, buf, 2, 0, 4))) == ALIGN      # batch stride not a multiple of 4
+    assert f(*args(osa.AttnMask(0, None, buf, 0, -4, 4))) == SHAPE     # negative stride
+    assert f(*args(osa.AttnMask(1, buf + 2, buf, 0, 0, 4))) == ALIGN   # kv_len checked too
 
 
 def test_masked_validation(L, buf):

@@ -100,3 +100,49 @@ def test_many_rows_and_in_place():
     y = xd.cpu().numpy().astype(np.float64)
     ref = oracle.softmax(x.astype(np.float64))
     assert np.max(np.abs(y - ref)) <= F32_TOL
+
+
+@pytest.mark.parametrize("n", [1, 3, 64, 260, 1000, 4096, 4097, 8192, 32768, 65536, 70000])
+def test_lse_matches_oracle(n):
+    # online_softmax_lse: softmax rows and their log-sum-exp together, and the
+    # log-sum-exp alone (one read of x), on every kernel path.
+    import torch
+
+    import online_softmax_10_amd as osa
+
+    rows = 37 if n <= 4096 else 5
+    x = si.make_rows(rows, n, seed=100 + n, spread=4.0)
+    x[0] += 500.0  # far above any exponent range: only differences enter
+    log(f"[gpu] online_softmax_lse rows={rows} n={n}")
+    xd = torch.from_numpy(x).cuda()
+    y, lse = osa.online_softmax(xd, return_lse=True)
+    lse_only = osa.logsumexp(xd)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    lse_only = lse_only.cpu().numpy().astype(np.float64)
+    ref_y = oracle.softmax(x.astype(np.float64))
+    ref_lse = oracle.logsumexp(x.astype(np.float64))
+    # fp32 rounding of an LSE grows with the size of the logits (as for the
+    # cross-entropy rows): 1e-5 scaled by max|x| / 8 when above 8.
+    tol = F32_TOL * np.maximum(1.0, np.abs(x).max(axis=1) / 8.0)
+    dl = np.abs(lse - ref_lse)
+    log(f"  max|dlse|={dl.max():.3e} (row bound {tol.min():.1e}..{tol.max():.1e}) max|dy|={np.abs(y - ref_y).max():.3e}")
+    assert np.all(dl <= tol)
+    assert np.array_equal(lse, lse_only), "the LSE alone must equal the LSE given with the softmax"
+    assert np.max(np.abs(y - ref_y)) <= F32_TOL
+
+
+def test_lse_of_neg_inf_row():
+    import torch
+
+    import online_softmax_10_amd as osa
+
+    x = si.make_rows(3, 100, seed=9)
+    x[1, :] = -np.inf
+    x[2, 5:] = -np.inf
+    log("[gpu] logsumexp with an all -inf row")
+    lse = osa.logsumexp(torch.from_numpy(x).cuda()).cpu().numpy().astype(np.float64)
+    assert np.isneginf(lse[1])
+    ref = oracle.logsumexp(x[[0, 2]].astype(np.float64))
+    assert np.max(np.abs(lse[[0, 2]] - ref)) <= F32_TOL
