@@ -11,9 +11,12 @@
 //   attn_fwd_bf16_kernel     4 waves, 128 query rows per workgroup, two
 //                            workgroups per CU (small problems, split partials);
 //   attn_fwd_bf16_w8_kernel  8 waves, 256 query rows per workgroup, one per CU
-//                            (problems whose 256-row tiles fill the chip), so a
-//                            K/V tile crosses L2 -> LDS once per 256 rows.
-// Either way each SIMD runs two waves.
+//                            (problems whose 256-row tiles fill the chip; single
+//                            pass), so a K/V tile crosses L2 -> LDS once per 256
+//                            rows.
+// Either way each SIMD runs two waves.  attn_fwd_bf16_bias_kernel is the
+// four-wave width with an additive score bias (one workgroup per CU at
+// d = 128, where its bias prefetch does not fit at two).
 //
 // Software pipeline.  Iteration j of a wave's key loop, with the scores
 // S(j) of tile j already in registers:
@@ -294,14 +297,18 @@ hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
     const uint16_t *q = static_cast<const uint16_t *>(p.q), *k = static_cast<const uint16_t *>(p.k),
                    *v = static_cast<const uint16_t *>(p.v);
     uint16_t *o = static_cast<uint16_t *>(p.o);
-    if (NW == 4 && p.bias != nullptr) {
+    if constexpr (NW == 8) {
+        hipLaunchKernelGGL((attn_fwd_bf16_w8_kernel<D, CAUSAL, SPLIT>), grid, dim3(512), 0, stream, q, k, v, o, p.lse,
+                           p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split,
+                           p.kv_len, p.H, p.causal_off);
+    } else if (p.bias != nullptr) {
         hipLaunchKernelGGL((attn_fwd_bf16_bias_kernel<D, CAUSAL, SPLIT>), grid, dim3(256), 0, stream, q, k, v, o,
                            p.lse, p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits,
                            p.tiles_per_split, p.kv_len, p.H, p.causal_off, p.bias, p.bias_sb, p.bias_sh, p.bias_sn);
     } else {
-        auto kernel = NW == 8 ? attn_fwd_bf16_w8_kernel<D, CAUSAL, SPLIT> : attn_fwd_bf16_kernel<D, CAUSAL, SPLIT>;
-        hipLaunchKernelGGL(kernel, grid, dim3(64 * NW), 0, stream, q, k, v, o, p.lse, p.part_o, p.part_lse, p.BH,
-                           p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split, p.kv_len, p.H, p.causal_off);
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, SPLIT>), grid, dim3(256), 0, stream, q, k, v, o, p.lse,
+                           p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split,
+                           p.kv_len, p.H, p.causal_off);
     }
     return hipGetLastError();
 }
@@ -321,8 +328,10 @@ hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream) {
-    // Single pass, no bias (the front end never asks this kernel for either).
-    return p.d == 64 ? launch_d<8, 64>(p, stream) : launch_d<8, 128>(p, stream);
+    // Single pass, no bias: the front end never asks this kernel for either.
+    if (p.splits != 1 || p.bias != nullptr) return hipErrorInvalidValue;
+    if (p.d == 64) return p.causal ? launch_t<8, 64, true, false>(p, stream) : launch_t<8, 64, false, false>(p, stream);
+    return p.causal ? launch_t<8, 128, true, false>(p, stream) : launch_t<8, 128, false, false>(p, stream);
 }
 
 }  // namespace osa
