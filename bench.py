@@ -56,10 +56,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel: str):
+def load_traffic(workload: str, kernel: str, path: str = ""):
     """HBM bytes per launch from the committed counter summary, if it covers this
     kernel and matches the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{workload}.json")
+    path = path or os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as f:
@@ -83,7 +83,7 @@ def counter_commands(wl: str) -> list:
             f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o run -- {cal}"]
 
 
-def traffic_from_counters(wl: str, kernel: str, out_dir: str) -> dict:
+def traffic_from_counters(wl: str, kernel: str, out_dir: str, dest: str = "") -> dict:
     """HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE runs (KiB
     per dispatch, first dispatch dropped), each scaled by what the same counter
     reads for a plain copy of known size; written to
@@ -126,7 +126,8 @@ def traffic_from_counters(wl: str, kernel: str, out_dir: str) -> dict:
         "note": "KiB per dispatch averaged over the timed dispatches (first excluded); factors = copied bytes / "
                 "counter bytes for a plain device copy",
     }
-    with open(os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{wl}.json"), "w", encoding="utf-8") as f:
+    dest = dest or os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{wl}.json")
+    with open(dest, "w", encoding="utf-8") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     return out
