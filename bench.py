@@ -459,7 +459,12 @@ def main() -> int:
         kernel, splits = "attn_kv_block_kernel (one launch per 64-key block)", 1
     abytes = algorithmic_bytes(w)
     if args.bias:
-        kernel = "attn_fwd_bf16_bias_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel"
+        # Bias calls take the bias instantiation of the width the plan names
+        # (never the decode kernel).
+        if w.dtype != "bf16":
+            kernel = "attn_fwd_f32_kernel"
+        else:
+            kernel = "attn_fwd_bf16_w8_bias_kernel" if kernel == "attn_fwd_bf16_w8_kernel" else "attn_fwd_bf16_bias_kernel"
         abytes += w.N * w.M * 4  # the broadcast bias, read once
     achieved = w.flops / (launch_ms * 1e-3) / 1e12
     peak = PEAKS_TFLOPS[w.dtype]

@@ -148,11 +148,13 @@ typedef struct attn_mask {
  *
  * Arguments and errors as attn_fwd_splits, plus ATTN_ERR_MASK for an unknown
  * causal mode, ATTN_ERR_ALIGN for a misaligned kv_len or bias (pointer or a
- * stride not a multiple of 4) and ATTN_ERR_SHAPE for a negative bias stride.
- * kv_len and bias are read by the kernels (asynchronously, on `stream`); they
- * are not validated on the host.  Calls with a bias run on the four-wave bf16
- * kernel (or the fp32 kernel), never the decode or eight-wave kernels, and
- * attn_fwd_plan does not describe them.
+ * stride not a multiple of 4), ATTN_ERR_SHAPE for a negative bias stride and
+ * ATTN_ERR_OVERFLOW when the bias spans 4 GiB or more from its base (the
+ * kernels address it with 32-bit offsets).  kv_len and bias are read by the
+ * kernels (asynchronously, on `stream`); they are not validated on the host.
+ * Calls with a bias run on the bias instantiations of the bf16 kernels (or
+ * the fp32 kernel), never the decode kernel, and attn_fwd_plan does not
+ * describe them.
  */
 int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse,
                     int64_t B, int64_t H, int64_t N, int64_t M, int d,

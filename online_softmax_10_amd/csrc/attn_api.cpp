@@ -98,17 +98,17 @@ int validate_attn(const void *q, const void *k, const void *v, const void *o, co
 
 // The kernel that carries the attention itself for a plan (the split paths
 // add the merge kernel).
-enum class MainKernel { F32, BF16_4W, BF16_8W, DECODE, BF16_BIAS };
+enum class MainKernel { F32, BF16_4W, BF16_8W, DECODE, BF16_BIAS, BF16_8W_BIAS };
 
 MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16, bool bias = false) {
     if (plan.kind == Plan::DECODE) return MainKernel::DECODE;
     if (!bf16) return MainKernel::F32;
-    if (bias) return MainKernel::BF16_BIAS;
     // The eight-wave kernel shares each K/V tile among 256 rows; use it for
     // single-pass problems whose 256-row tiles alone give every compute unit
     // a workgroup.
-    if (plan.kind == Plan::SINGLE && BH * ceil_div(N, osa::kBf16WideRows) >= 256) return MainKernel::BF16_8W;
-    return MainKernel::BF16_4W;
+    if (plan.kind == Plan::SINGLE && BH * ceil_div(N, osa::kBf16WideRows) >= 256)
+        return bias ? MainKernel::BF16_8W_BIAS : MainKernel::BF16_8W;
+    return bias ? MainKernel::BF16_BIAS : MainKernel::BF16_4W;
 }
 
 const char *main_kernel_name(MainKernel k) {
@@ -118,6 +118,7 @@ const char *main_kernel_name(MainKernel k) {
     case MainKernel::BF16_8W: return "attn_fwd_bf16_w8_kernel";
     case MainKernel::DECODE: return "attn_decode_kernel";
     case MainKernel::BF16_BIAS: return "attn_fwd_bf16_bias_kernel";
+    case MainKernel::BF16_8W_BIAS: return "attn_fwd_bf16_w8_bias_kernel";
     }
     return "";
 }
@@ -148,6 +149,11 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
         p.bias_sb = mask->bias_stride_b;
         p.bias_sh = mask->bias_stride_h;
         p.bias_sn = mask->bias_stride_n;
+        // The kernels address the bias with 32-bit byte offsets from its base.
+        const double extent = 4.0 * ((double)(B - 1) * p.bias_sb + (double)(H - 1) * p.bias_sh +
+                                     (double)(N - 1) * p.bias_sn + (double)M);
+        if (extent > 4294967296.0 - 4096.0) return ATTN_ERR_OVERFLOW;
+        p.bias_bytes = (uint32_t)extent;
     }
     p.causal_off = causal == ATTN_CAUSAL_BOTTOM_RIGHT ? (int)(M - N) : 0;
     // Scores are kept in base-2 units.  c is at least the smallest normal float
@@ -165,9 +171,10 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     p.tiles_per_split = plan.tiles_per_split;
     if (plan.kind == Plan::SINGLE) {
         p.tiles_per_split = ceil_div(M, bf16 ? osa::kBf16KeyTile : osa::kF32KeyTile);
-        const hipError_t e = kernel == MainKernel::F32       ? osa::launch_attn_f32(p, stream)
-                             : kernel == MainKernel::BF16_8W ? osa::launch_attn_bf16_w8(p, stream)
-                                                             : osa::launch_attn_bf16(p, stream);
+        const bool w8 = kernel == MainKernel::BF16_8W || kernel == MainKernel::BF16_8W_BIAS;
+        const hipError_t e = kernel == MainKernel::F32 ? osa::launch_attn_f32(p, stream)
+                             : w8                      ? osa::launch_attn_bf16_w8(p, stream)
+                                                       : osa::launch_attn_bf16(p, stream);
         if (e != hipSuccess) {
             set_detail("attention kernel launch", e);
             return ATTN_ERR_HIP;

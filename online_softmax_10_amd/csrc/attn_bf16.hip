@@ -57,8 +57,8 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
                                           float *__restrict__ part_lse, int BH, int N, int M, float c,
                                           uint32_t qsign, int ntq, int splits, int tiles_per_split,
                                           const int32_t *__restrict__ kv_len, int H, int coff,
-                                          const float *__restrict__ bias, int64_t bias_sb, int64_t bias_sh,
-                                          int64_t bias_sn) {
+                                          const float *__restrict__ bias, uint32_t bias_bytes, int64_t bias_sb,
+                                          int64_t bias_sh, int64_t bias_sn) {
     using T = Tile<D>;
     constexpr int BR = 32 * NW;           // query rows per workgroup
     constexpr int LOADS = T::LOADS / NW;  // LDS-direct loads per wave per tile, for K and for V
@@ -99,11 +99,18 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     // before the tile math, which then runs with c = 1.
     WaveTile<D, CAUSAL> wt;
     wt.init(q + (size_t)bh * N * D, N, q0 + wave * 32, lane, BIAS ? 1.f : c, qsign, coff);
-    const float *brow = nullptr;  // this lane's bias row (rows past N read row N - 1)
-    f32x4 bnext[8];               // bias of the next tile this wave computes
-    if constexpr (BIAS)
-        brow = bias + (int64_t)(bh / H) * bias_sb + (int64_t)(bh % H) * bias_sh +
-               (int64_t)min(wt.qrow, N - 1) * bias_sn;
+    // This lane's bias row as a byte offset into the bias buffer (rows past N
+    // read row N - 1); the front end keeps the bias extent below 2^32 bytes.
+    u32x4 brs{};
+    uint32_t brow = 0;
+    char *bregion = nullptr;  // this wave's 8 KiB bias stage in LDS
+    if constexpr (BIAS) {
+        __shared__ __attribute__((aligned(1024))) char lds_b[NW * 8192];
+        bregion = lds_b + wave * 8192;
+        brs = make_rsrc(bias, bias_bytes);
+        brow = 4u * (uint32_t)((int64_t)(bh / H) * bias_sb + (int64_t)(bh % H) * bias_sh +
+                               (int64_t)min(wt.qrow, N - 1) * bias_sn);
+    }
 
     int ld_off[LOADS];
 #pragma unroll
@@ -121,13 +128,13 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     // its share of K(j+2) and V(j+1) into the stages every wave has finished
     // with.  Load tile indices past the last are clamped to it: a harmless
     // reload into a free stage that keeps the block free of branches.
-    auto iteration = [&](auto full, auto loads, int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+    // bias_next: this wave computes tile j+2 too (its bias is fetched here).
+    auto iteration = [&](auto full, auto loads, int j, bool bias_next, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                          const char *ks_next, char *ks_free, const char *vs_cur, char *vs_free) {
         constexpr bool FULL = decltype(full)::value;
         constexpr bool LOADS_ON = decltype(loads)::value;
         wait_loads_and_barrier<0>();
-        if constexpr (BIAS) wt.apply_bias(bnext, s_cur, c);  // tile j's bias landed with the wait above
-        wt.mask(kb + j * BC, ke, s_cur);
+        wt.mask(kb + j * BC, ke, s_cur);  // s_cur holds the bias already (added during the last P.V phase)
         const float m = wt.m_run;
         uint32_t popw[BC / 16][4];
         float lsum0 = 0.f, lsum1 = 0.f;
@@ -169,9 +176,6 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         float alpha = 1.f;
         if (__builtin_amdgcn_ballot_w64(!(lsum <= SHIFT_SUM_LIMIT)) != 0) alpha = wt.exact_shift(s_cur, pop, lsum);
         wt.l_run = alpha * wt.l_run + lsum;
-        // Tile j+1's bias, over the P.V phase (its registers are free once the
-        // scores of tile j are packed into pop).
-        if constexpr (BIAS && FULL) wt.bias_fetch(brow, kb + (j + 1) * BC, M, bnext);
 
         bf16x8 vop[3];
         vop[0] = wt.vread(vs_cur, 0);
@@ -182,6 +186,21 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             const int t4 = slot / (D / 32), db = slot % (D / 32);
             wt.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[slot % 3], pop[t4], wt.oacc[db], 0, 0, 0);
             if (slot + 2 < PSLOTS) vop[(slot + 2) % 3] = wt.vread(vs_cur, slot + 2);
+            // The VALU is free here: the bias of tile j+1 (staged during the
+            // last iteration, landed with this iteration's wait) goes into its
+            // scores, run by run; then tile j+2's bias is fetched into the
+            // same region, once every read of it has returned.
+            if constexpr (BIAS && FULL) {
+                constexpr int PER = (8 + PSLOTS / 2 - 1) / (PSLOTS / 2);  // runs per slot over the first half
+                if (slot < PSLOTS / 2) {
+#pragma unroll
+                    for (int t = slot * PER; t < slot * PER + PER && t < 8; ++t) wt.bias_apply(bregion, t, lane, s_nxt, c);
+                }
+                if (slot == PSLOTS / 2 && bias_next) {
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    wt.bias_dma(brs, brow, kb + (j + 2) * BC, bregion);
+                }
+            }
             fence();
         }
     };
@@ -205,6 +224,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         nw = __builtin_amdgcn_readfirstlane(nw);
     }
 
+
     if (ntiles > 0) {
         // Prologue: K(0), V(0) land; S(0) is computed while K(1) loads.
 #pragma unroll
@@ -212,7 +232,9 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             load(krs, 0, lds_k0, i);
             load(vrs, 0, lds_v0, i);
         }
-        if constexpr (BIAS) wt.bias_fetch(brow, kb, M, bnext);
+        if constexpr (BIAS) {
+            if (nw > 0) wt.bias_dma(brs, brow, kb, bregion);
+        }
         wait_loads_and_barrier<0>();
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) load(krs, min(1, ntiles - 1), lds_k1, i);
@@ -223,19 +245,28 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         if (nw > 0) {
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) wt.score_step(lds_k0, kk, sa);
+            if constexpr (BIAS) {
+                // Tile 0's bias landed with the prologue's wait; tile 1's follows.
+#pragma unroll
+                for (int t = 0; t < 8; ++t) wt.bias_apply(bregion, t, lane, sa, c);
+                if (nw > 1) {
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    wt.bias_dma(brs, brow, kb + BC, bregion);
+                }
+            }
             for (; j + 2 < nw; j += 2) {
-                iteration(Full{}, LoadsOn{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
-                iteration(Full{}, LoadsOn{}, j + 1, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+                iteration(Full{}, LoadsOn{}, j, true, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+                iteration(Full{}, LoadsOn{}, j + 1, j + 3 < nw, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
             }
             // This wave's last tile: loads still go on while the workgroup has more.
             if (j + 2 == nw) {
-                iteration(Full{}, LoadsOn{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+                iteration(Full{}, LoadsOn{}, j, false, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
                 ++j;
-                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
-                else iteration(Last{}, LoadsOff{}, j, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, false, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+                else iteration(Last{}, LoadsOff{}, j, false, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
             } else {
-                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
-                else iteration(Last{}, LoadsOff{}, j, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, false, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+                else iteration(Last{}, LoadsOff{}, j, false, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
             }
             ++j;
         }
@@ -270,22 +301,26 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(ATTN_KERNEL_ARGS) {
-    attn_body<4, D, CAUSAL, SPLIT, false>(ATTN_KERNEL_PASS, nullptr, 0, 0, 0);
+    attn_body<4, D, CAUSAL, SPLIT, false>(ATTN_KERNEL_PASS, nullptr, 0u, 0, 0, 0);
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_w8_kernel(ATTN_KERNEL_ARGS) {
-    attn_body<8, D, CAUSAL, SPLIT, false>(ATTN_KERNEL_PASS, nullptr, 0, 0, 0);
+    attn_body<8, D, CAUSAL, SPLIT, false>(ATTN_KERNEL_PASS, nullptr, 0u, 0, 0, 0);
 }
 
-// The four-wave kernel with an additive score bias.  The bias prefetch takes
-// 32 more registers per lane: at d = 128 that exceeds the 256 of two
-// workgroups per CU, so there the kernel runs one workgroup per CU.
+// Both widths with an additive score bias (staged through 8 KiB of LDS per
+// wave: at d = 128 the four-wave width then fits one workgroup per CU).
+#define ATTN_BIAS_ARGS \
+    ATTN_KERNEL_ARGS, const float *__restrict__ bias, uint32_t bias_bytes, int64_t bias_sb, int64_t bias_sh, int64_t bias_sn
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_fwd_bf16_bias_kernel(ATTN_KERNEL_ARGS, const float *__restrict__ bias,
-                                                                    int64_t bias_sb, int64_t bias_sh,
-                                                                    int64_t bias_sn) {
-    attn_body<4, D, CAUSAL, SPLIT, true>(ATTN_KERNEL_PASS, bias, bias_sb, bias_sh, bias_sn);
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_bias_kernel(ATTN_BIAS_ARGS) {
+    attn_body<4, D, CAUSAL, SPLIT, true>(ATTN_KERNEL_PASS, bias, bias_bytes, bias_sb, bias_sh, bias_sn);
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_w8_bias_kernel(ATTN_BIAS_ARGS) {
+    attn_body<8, D, CAUSAL, SPLIT, true>(ATTN_KERNEL_PASS, bias, bias_bytes, bias_sb, bias_sh, bias_sn);
 }
 
 template <int NW, int D, bool CAUSAL, bool SPLIT>
@@ -297,14 +332,21 @@ hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
     const uint16_t *q = static_cast<const uint16_t *>(p.q), *k = static_cast<const uint16_t *>(p.k),
                    *v = static_cast<const uint16_t *>(p.v);
     uint16_t *o = static_cast<uint16_t *>(p.o);
-    if constexpr (NW == 8) {
+    if (p.bias != nullptr) {
+        if constexpr (NW == 8)
+            hipLaunchKernelGGL((attn_fwd_bf16_w8_bias_kernel<D, CAUSAL, SPLIT>), grid, dim3(512), 0, stream, q, k, v, o,
+                               p.lse, p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits,
+                               p.tiles_per_split, p.kv_len, p.H, p.causal_off, p.bias, p.bias_bytes, p.bias_sb,
+                               p.bias_sh, p.bias_sn);
+        else
+            hipLaunchKernelGGL((attn_fwd_bf16_bias_kernel<D, CAUSAL, SPLIT>), grid, dim3(256), 0, stream, q, k, v, o,
+                               p.lse, p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits,
+                               p.tiles_per_split, p.kv_len, p.H, p.causal_off, p.bias, p.bias_bytes, p.bias_sb,
+                               p.bias_sh, p.bias_sn);
+    } else if constexpr (NW == 8) {
         hipLaunchKernelGGL((attn_fwd_bf16_w8_kernel<D, CAUSAL, SPLIT>), grid, dim3(512), 0, stream, q, k, v, o, p.lse,
                            p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split,
                            p.kv_len, p.H, p.causal_off);
-    } else if (p.bias != nullptr) {
-        hipLaunchKernelGGL((attn_fwd_bf16_bias_kernel<D, CAUSAL, SPLIT>), grid, dim3(256), 0, stream, q, k, v, o,
-                           p.lse, p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits,
-                           p.tiles_per_split, p.kv_len, p.H, p.causal_off, p.bias, p.bias_sb, p.bias_sh, p.bias_sn);
     } else {
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, SPLIT>), grid, dim3(256), 0, stream, q, k, v, o, p.lse,
                            p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits, p.tiles_per_split,
@@ -328,8 +370,8 @@ hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream) {
-    // Single pass, no bias: the front end never asks this kernel for either.
-    if (p.splits != 1 || p.bias != nullptr) return hipErrorInvalidValue;
+    // Single pass only: the front end never asks this width for partials.
+    if (p.splits != 1) return hipErrorInvalidValue;
     if (p.d == 64) return p.causal ? launch_t<8, 64, true, false>(p, stream) : launch_t<8, 64, false, false>(p, stream);
     return p.causal ? launch_t<8, 128, true, false>(p, stream) : launch_t<8, 128, false, false>(p, stream);
 }

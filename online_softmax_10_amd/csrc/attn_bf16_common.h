@@ -217,35 +217,30 @@ struct WaveTile {
         }
     }
 
-    // Additive bias: the 32 bias values of this lane's scores of the tile at
-    // kv0 (register r of block cb is key kv0 + 32*cb + 16*(r/8) + 8*hh + r%8:
-    // two runs of four), from the bias row of its query.  Keys at or past M
-    // read as 0 (they are masked).
-    __device__ __forceinline__ void bias_fetch(const float *brow, int kv0, int M, f32x4 (&b)[8]) const {
+    // Additive bias, staged through an 8 KiB LDS region of this wave.  The
+    // 32 bias values of a lane's scores of the tile at kv0 form eight runs of
+    // four keys (register r of block cb is key kv0 + 32*cb + 16*(r/8) + 8*hh
+    // + r%8, so run t = 4*cb + 2*(r/8) + (r%8)/4); LDS-direct load t has every
+    // lane fetch its own run t from its query's bias row (byte offset row_off
+    // in the buffer brs), which lands at region + 1024*t + 16*lane.  The
+    // buffer's range check returns 0 past the bias (those keys are masked).
+    __device__ __forceinline__ void bias_dma(const u32x4 &brs, uint32_t row_off, int kv0, char *region) const {
 #pragma unroll
-        for (int run = 0; run < 8; ++run) {
-            const int key = kv0 + 32 * (run >> 2) + 16 * ((run >> 1) & 1) + 8 * hh + 4 * (run & 1);
-            if (key + 4 <= M) {
-                b[run] = *reinterpret_cast<const f32x4 *>(brow + key);
-            } else {
-                f32x4 x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = key + e < M ? brow[key + e] : 0.f;
-                b[run] = x;
-            }
+        for (int t = 0; t < 8; ++t) {
+            const int key = kv0 + 32 * (t >> 2) + 16 * ((t >> 1) & 1) + 8 * hh + 4 * (t & 1);
+            lds_direct_load16(brs, lds_addr(region + 1024 * t), (int)(row_off + 4u * (uint32_t)key));
         }
     }
 
-    // s <- c_scale * s + log2(e) * bias: scores in base-2 units with the bias
-    // added (the tile math then runs with c = 1).
-    __device__ __forceinline__ void apply_bias(const f32x4 (&b)[8], f32x16 (&s)[2], float c_scale) const {
+    // Run t of the staged bias into s: s <- c_scale * s + log2(e) * bias, the
+    // scores in base-2 units with the bias added (the tile math then runs
+    // with c = 1).
+    __device__ __forceinline__ void bias_apply(const char *region, int t, int lane, f32x16 (&s)[2],
+                                               float c_scale) const {
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(region + 1024 * t + 16 * lane);
+        const int cb = t >> 2, r0 = 8 * ((t >> 1) & 1) + 4 * (t & 1);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int run = 4 * cb + 2 * (r >> 3) + ((r & 7) >> 2);
-                s[cb][r] = __builtin_fmaf(s[cb][r], c_scale, b[run][r & 3] * LOG2E);
-            }
+        for (int e = 0; e < 4; ++e) s[cb][r0 + e] = __builtin_fmaf(s[cb][r0 + e], c_scale, b[e] * LOG2E);
     }
 
     // P = 2^(c*s - m) for shift m, rounded to bf16 as the operands of P.V;

@@ -18,6 +18,7 @@ struct AttnProblem {
     // Additive score bias, fp32, or nullptr: element (b, h, i, j) at
     // bias[b*bias_sb + h*bias_sh + i*bias_sn + j]; 16-byte aligned rows.
     const float *bias;
+    uint32_t bias_bytes;     // bytes from bias to the end of its last element (< 2^32)
     int64_t bias_sb, bias_sh, bias_sn;
     int causal_off;          // causal: key j visible for query i iff j <= i + causal_off
     float c;                 // |scale| * log2(e): scores are kept in base-2 units
