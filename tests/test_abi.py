@@ -200,6 +200,10 @@ def test_bias_validation(L, buf):
     assert f(*args(osa.AttnMask(0, None, buf, 2, 0, 4))) == ALIGN      # batch stride not a multiple of 4
     assert f(*args(osa.AttnMask(0, None, buf, 0, -4, 4))) == SHAPE     # negative stride
     assert f(*args(osa.AttnMask(1, buf + 2, buf, 0, 0, 4))) == ALIGN   # kv_len checked too
+    # A bias spanning 4 GiB or more from its base (32-bit offsets in the kernels).
+    big = lambda sb: (buf, buf, buf, buf, buf, 2, 1, 4, 4, 64, 0.125,
+                      ctypes.byref(osa.AttnMask(0, None, buf, sb, 0, 4)), 1, 0, None)
+    assert f(*big(2**30)) == OVERFLOW
 
 
 def test_masked_validation(L, buf):
