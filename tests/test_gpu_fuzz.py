@@ -1,0 +1,68 @@
+"""Seeded random problems against the float64 oracle: batch, heads, query and
+key counts, head size, dtype, causal alignment, key lengths, an additive bias
+(full or broadcast) and the split count drawn independently per case, so
+combinations no hand-written case covers still meet the tolerance rule."""
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from parity import compare, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+CASES = 48
+
+
+def draw(case: int):
+    rng = np.random.default_rng(9000 + case)
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    N = int(rng.choice([int(rng.integers(1, 6)), int(rng.integers(1, 300)), int(rng.integers(300, 700))]))
+    M = int(rng.choice([int(rng.integers(1, 70)), int(rng.integers(64, 400)), int(rng.integers(400, 1100))]))
+    d = int(rng.choice([64, 128]))
+    dtype = "f32" if rng.random() < 0.25 else "bf16"
+    causal = [False, True, "bottom_right"][int(rng.integers(0, 3))]
+    kv_len = [int(x) for x in rng.integers(0, M + 1, size=B)] if rng.random() < 0.4 else None
+    bias = None
+    r = rng.random()
+    if r < 0.2:
+        bias = (B, H, N, M)
+    elif r < 0.35:
+        bias = (N, M)
+    elif r < 0.45:
+        bias = (1, H, 1, M)
+    splits = int(rng.choice([0, 0, 1, 2, 5]))
+    dist = ["normal", "uniform01", "normal_qk3"][int(rng.integers(0, 3))]
+    return si.Workload("fuzz", B, H, N, M, d, dtype, causal is not False, dist), causal, kv_len, bias, splits
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_problem(case):
+    import torch
+
+    import online_softmax_10_amd as osa
+
+    w, causal, kv_len, bshape, splits = draw(case)
+    log(f"[gpu] fuzz {case}: B={w.B} H={w.H} N={w.N} M={w.M} d={w.d} {w.dtype} {w.dist} causal={causal} "
+        f"kv_len={kv_len} bias={bshape} splits={splits}")
+    q, k, v = si.make_qkv(w, case)
+    bias = None if bshape is None else si.make_bias(bshape, case + 500, "normal", 0.05)
+    qd, kd, vd = (to_device(a, w.dtype) for a in (q, k, v))
+    kl = None if kv_len is None else torch.tensor(kv_len, dtype=torch.int32, device="cuda")
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    o, lse = osa.fwd_splits(qd, kd, vd, scale=w.scale, causal=causal, num_splits=splits, kv_len=kl, bias=bd)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = oracle.attention(si.to_f64(q, w.dtype), si.to_f64(k, w.dtype), si.to_f64(v, w.dtype), w.scale,
+                                      causal, kv_len=kv_len, bias=None if bias is None else bias.astype(np.float64))
+    vis = np.isfinite(lse_ref)
+    assert np.all(o[~vis] == 0.0) and np.all(np.isneginf(lse[~vis])), "rows with no finite score"
+    if vis.any():
+        # fp32 bound scaled by the largest scaled logit (bias included), as for the other fp32 stress cases
+        s = np.einsum("bhnd,bhmd->bhnm", si.to_f64(q, w.dtype), si.to_f64(k, w.dtype)) * w.scale
+        if bias is not None:
+            s = s + np.broadcast_to(bias.astype(np.float64), s.shape)
+        logit_max = float(np.max(np.abs(s[np.isfinite(s)]))) if np.isfinite(s).any() else 8.0
+        compare(o[vis], lse[vis], o_ref[vis], lse_ref[vis], w.dtype, f"fuzz {case}", logit_max=max(8.0, logit_max))
