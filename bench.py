@@ -49,10 +49,15 @@ def err(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention sources' code: // comments, trailing blanks and
+    empty lines are dropped, so a comment-only edit keeps the stamp."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "online_softmax_10_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "online_softmax_10_amd", "csrc", name), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode("utf-8") + b"\n")
     return h.hexdigest()[:16]
 
 

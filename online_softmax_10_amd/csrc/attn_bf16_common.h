@@ -30,6 +30,10 @@
 // wave take the exact path: row max, new shift, rescale of l and o~, and the
 // probabilities again.  Any shift gives the same softmax as long as numerator
 // and denominator share it and nothing overflows.
+//
+// An additive score bias (an elementwise mask(), which eq. (8) leaves open)
+// is staged through LDS per wave and folded into the scores as
+// c * s + log2(e) * bias before the tile math, which then runs with c = 1.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -72,6 +72,19 @@ def test_traffic_from_counters(tmp_path):
     assert bench.load_traffic("c3", k, dest) is None
 
 
+def test_source_stamp_ignores_comments(tmp_path, monkeypatch):
+    src = tmp_path / "online_softmax_10_amd" / "csrc"
+    src.mkdir(parents=True)
+    for name in bench.KERNEL_SOURCES:
+        (src / name).write_text("int a = 1;  // one\n\n// note\nint b = 2;\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    (src / bench.KERNEL_SOURCES[0]).write_text("int a = 1;  // another note\n// more\nint b = 2;   \n")
+    assert bench.kernel_source_hash() == h0
+    (src / bench.KERNEL_SOURCES[0]).write_text("int a = 1;\nint b = 3;\n")
+    assert bench.kernel_source_hash() != h0
+
+
 def test_committed_traffic_matches_the_sources():
     # The committed counter summaries were taken on the current kernels.
     for wl in ("c3", "c4"):
