@@ -25,8 +25,9 @@ extern "C" {
 
 /* Element type of q, k, v and o. */
 typedef enum {
-    ATTN_F32 = 0,  /* IEEE binary32 */
-    ATTN_BF16 = 1  /* bfloat16 (8-bit significand), stored as 16-bit words */
+    ATTN_F32 = 0,          /* IEEE binary32 */
+    ATTN_BF16 = 1,         /* bfloat16 (8-bit significand), stored as 16-bit words */
+    ATTN_BF16_OUT_F32 = 2  /* q, k, v bfloat16 as ATTN_BF16; o float32 (not rounded to bf16) */
 } attn_dtype;
 
 /* Return codes. */
@@ -75,9 +76,11 @@ enum {
  *   d      head dim, 64 or 128 (compile-time instantiations)
  *   scale  finite float32 used exactly as passed (1/sqrt(d) for the usual form)
  *   causal 0 or non-zero
- *   dtype  ATTN_F32 (fp32 products and accumulation throughout) or ATTN_BF16
+ *   dtype  ATTN_F32 (fp32 products and accumulation throughout), ATTN_BF16
  *          (bf16 products, fp32 accumulation, probabilities rounded to bf16
- *          before the P.V product, o rounded to nearest-even bf16)
+ *          before the P.V product, o rounded to nearest-even bf16) or
+ *          ATTN_BF16_OUT_F32 (the same arithmetic with o written as float32:
+ *          the output keeps the fp32 accumulation's precision)
  *   stream hipStream_t as void*
  * o must not overlap q, k, v or lse.  q, k, v, o and lse must be 16-byte
  * aligned.  Per-head sizes N*d and M*d must each be below 2^31 elements and

@@ -17,12 +17,13 @@ import math
 import os
 
 __all__ = ["fwd", "fwd_splits", "fwd_kv_outer", "online_softmax", "logsumexp", "softmax_xent", "plan", "lib", "AttnMask", "CAUSAL_MODES", "LIB_PATH", "AttnError",
-           "ATTN_F32", "ATTN_BF16", "ATTN_MAX_SPLITS", "EXPORTED_SYMBOLS"]
+           "ATTN_F32", "ATTN_BF16", "ATTN_BF16_OUT_F32", "ATTN_MAX_SPLITS", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_F32 = 0
 ATTN_BF16 = 1
+ATTN_BF16_OUT_F32 = 2
 ATTN_MAX_SPLITS = 256
 ERROR_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
                -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_OVERFLOW", -7: "ATTN_ERR_HIP",
@@ -145,7 +146,8 @@ def _bias_operand(bias, B, H, N, M, device):
     return view, st[:3]
 
 
-def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None, kv_len=None, bias=None):
+def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None, kv_len=None, bias=None,
+               out_dtype=None):
     """Attention forward with an explicit split count (0 = library's choice).
 
     q [B,H,N,d], k and v [B,H,M,d]: contiguous CUDA/HIP tensors of one dtype
@@ -153,9 +155,11 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
     query i when j > i) or "bottom_right" (when j > i + M - N).  kv_len:
     optional contiguous int32 GPU tensor [B] of valid key counts (keys j >=
     kv_len[b] masked).  bias: optional float32 GPU tensor broadcastable to
-    [B,H,N,M], added to the scaled scores (-inf masks a key).  Returns
-    (o [B,H,N,d] same dtype, lse [B,H,N] float32); a row with no visible key
-    (or only -inf scores) gets o = 0, lse = -inf.
+    [B,H,N,M], added to the scaled scores (-inf masks a key).  out_dtype:
+    torch.float32 with bfloat16 inputs writes o in float32 (the same
+    arithmetic, o not rounded to bf16); default: the inputs' dtype.  Returns
+    (o [B,H,N,d], lse [B,H,N] float32); a row with no visible key (or only
+    -inf scores) gets o = 0, lse = -inf.
     """
     import torch
 
@@ -171,14 +175,19 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
     code = _dtype_code(q)
+    o_dtype = q.dtype if out_dtype is None else out_dtype
+    if o_dtype != q.dtype:
+        if q.dtype != torch.bfloat16 or o_dtype != torch.float32:
+            raise ValueError("out_dtype other than the inputs' is only float32 with bfloat16 inputs")
+        code = ATTN_BF16_OUT_F32
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k, v must be on one device")
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
     else:
-        _check_output("out", out, (B, H, N, d), q.dtype, q.device)
+        _check_output("out", out, (B, H, N, d), o_dtype, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     else:
@@ -209,13 +218,13 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
     return out, lse
 
 
-def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None, bias=None):
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, kv_len=None, bias=None, out_dtype=None):
     """softmax(mask(q k^T * scale + bias)) v and the row log-sum-exp (natural log).
 
-    causal, kv_len and bias as in fwd_splits.
+    causal, kv_len, bias and out_dtype as in fwd_splits.
     """
     return fwd_splits(q, k, v, scale=scale, causal=causal, num_splits=0, out=out, lse=lse, kv_len=kv_len,
-                      bias=bias)
+                      bias=bias, out_dtype=out_dtype)
 
 
 def fwd_kv_outer(q, k, v, scale=None, causal=False, out=None, lse=None):

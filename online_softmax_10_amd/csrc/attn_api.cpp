@@ -82,7 +82,7 @@ int validate_attn(const void *q, const void *k, const void *v, const void *o, co
         if (!aligned16(mask->bias) || ((mask->bias_stride_b | mask->bias_stride_h | mask->bias_stride_n) & 3))
             return ATTN_ERR_ALIGN;
     }
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_BF16_OUT_F32) return ATTN_ERR_DTYPE;
     if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
     if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SPLITS;
@@ -100,9 +100,12 @@ int validate_attn(const void *q, const void *k, const void *v, const void *o, co
 // add the merge kernel).
 enum class MainKernel { F32, BF16_4W, BF16_8W, DECODE, BF16_BIAS, BF16_8W_BIAS };
 
-MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16, bool bias = false) {
+MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16, bool bias = false, bool out_f32 = false) {
     if (plan.kind == Plan::DECODE) return MainKernel::DECODE;
     if (!bf16) return MainKernel::F32;
+    // fp32 output with a bias: the four-wave width (its partial-store form
+    // fits the registers; the eight-wave one would spill).
+    if (bias && out_f32) return MainKernel::BF16_BIAS;
     // The eight-wave kernel shares each K/V tile among 256 rows; use it for
     // single-pass problems whose 256-row tiles alone give every compute unit
     // a workgroup.
@@ -128,7 +131,7 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     const int rc = validate_attn(q, k, v, o, lse, B, H, N, M, d, scale, dtype, num_splits, mask);
     if (rc != ATTN_OK || B == 0 || H == 0 || N == 0) return rc;
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
-    const bool bf16 = dtype == ATTN_BF16;
+    const bool bf16 = dtype != ATTN_F32;
     const int64_t BH = B * H;
 
     osa::AttnProblem p{};
@@ -162,15 +165,21 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     p.c = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
     p.negate_q = signbit(scale) != 0;
     p.causal = causal != ATTN_CAUSAL_NONE;
+    p.out_f32 = dtype == ATTN_BF16_OUT_F32;
 
     const Plan plan = plan_for(BH, N, M, bf16, num_splits, p.bias != nullptr);
     const int64_t blocks = plan.kind == Plan::DECODE ? BH * plan.splits : BH * ceil_div(N, 128) * plan.splits;
     if (blocks > kMaxBlocks) return ATTN_ERR_OVERFLOW;
-    const MainKernel kernel = main_kernel(plan, BH, N, bf16, p.bias != nullptr);
+    const MainKernel kernel = main_kernel(plan, BH, N, bf16, p.bias != nullptr, p.out_f32);
     p.splits = plan.splits;
     p.tiles_per_split = plan.tiles_per_split;
     if (plan.kind == Plan::SINGLE) {
         p.tiles_per_split = ceil_div(M, bf16 ? osa::kBf16KeyTile : osa::kF32KeyTile);
+        if (p.out_f32) {
+            // One "split" whose normalised fp32 partial and LSE are the outputs.
+            p.part_o = static_cast<float *>(o);
+            p.part_lse = lse;
+        }
         const bool w8 = kernel == MainKernel::BF16_8W || kernel == MainKernel::BF16_8W_BIAS;
         const hipError_t e = kernel == MainKernel::F32 ? osa::launch_attn_f32(p, stream)
                              : w8                      ? osa::launch_attn_bf16_w8(p, stream)
@@ -199,7 +208,7 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     else
         e = kernel == MainKernel::F32 ? osa::launch_attn_f32(p, stream) : osa::launch_attn_bf16(p, stream);
     if (e == hipSuccess) {
-        e = osa::launch_split_merge(p, bf16, stream);
+        e = osa::launch_split_merge(p, bf16 && !p.out_f32, stream);
         if (e != hipSuccess) set_detail("split merge kernel launch", e);
     } else {
         set_detail("split attention kernel launch", e);
@@ -323,11 +332,11 @@ const char *attn_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int d, int
                           int *splits) {
     if (splits) *splits = 0;
     if (B < 1 || H < 1 || N < 1 || M < 1) return nullptr;
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return nullptr;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_BF16_OUT_F32) return nullptr;
     if (d != 64 && d != 128) return nullptr;
     if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return nullptr;
     if (B > kI32Max || H > kI32Max || B * H > kI32Max || N > kI32Max / d || M > kI32Max / d) return nullptr;
-    const bool bf16 = dtype == ATTN_BF16;
+    const bool bf16 = dtype != ATTN_F32;
     const Plan plan = plan_for(B * H, N, M, bf16, num_splits);
     if (splits) *splits = plan.splits;
     return main_kernel_name(main_kernel(plan, B * H, N, bf16));
@@ -339,7 +348,7 @@ const char *attn_strerror(int code) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid shape (negative size, or M < 1 / n < 1 with work to do)";
     case ATTN_ERR_HEADDIM: return "unsupported head dim (compiled for d = 64 and d = 128)";
-    case ATTN_ERR_DTYPE: return "unsupported dtype (ATTN_F32 or ATTN_BF16)";
+    case ATTN_ERR_DTYPE: return "unsupported dtype (ATTN_F32, ATTN_BF16 or ATTN_BF16_OUT_F32)";
     case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
     case ATTN_ERR_OVERFLOW: return "sizes exceed the kernels' index range";
     case ATTN_ERR_HIP: return "HIP launch or allocation failed";

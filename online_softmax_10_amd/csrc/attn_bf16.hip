@@ -333,7 +333,9 @@ hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
                    *v = static_cast<const uint16_t *>(p.v);
     uint16_t *o = static_cast<uint16_t *>(p.o);
     if (p.bias != nullptr) {
-        if constexpr (NW == 8)
+        if constexpr (NW == 8 && SPLIT)
+            return hipErrorInvalidValue;  // never asked: partials with a bias take the four-wave width
+        else if constexpr (NW == 8)
             hipLaunchKernelGGL((attn_fwd_bf16_w8_bias_kernel<D, CAUSAL, SPLIT>), grid, dim3(512), 0, stream, q, k, v, o,
                                p.lse, p.part_o, p.part_lse, p.BH, p.N, p.M, p.c, qsign, ntq, p.splits,
                                p.tiles_per_split, p.kv_len, p.H, p.causal_off, p.bias, p.bias_bytes, p.bias_sb,
@@ -357,7 +359,8 @@ hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
 
 template <int NW, int D>
 hipError_t launch_d(const AttnProblem &p, hipStream_t stream) {
-    const bool split = p.splits > 1;
+    // The partial-store form also writes a float32 o (one split).
+    const bool split = p.splits > 1 || p.out_f32;
     if (p.causal) return split ? launch_t<NW, D, true, true>(p, stream) : launch_t<NW, D, true, false>(p, stream);
     return split ? launch_t<NW, D, false, true>(p, stream) : launch_t<NW, D, false, false>(p, stream);
 }
@@ -370,8 +373,13 @@ hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream) {
-    // Single pass only: the front end never asks this width for partials.
-    if (p.splits != 1) return hipErrorInvalidValue;
+    // Single pass only (a float32 o through the partial-store form, without a
+    // bias): the front end never asks this width for split partials.
+    if (p.splits != 1 || (p.out_f32 && p.bias != nullptr)) return hipErrorInvalidValue;
+    if (p.out_f32) {
+        if (p.d == 64) return p.causal ? launch_t<8, 64, true, true>(p, stream) : launch_t<8, 64, false, true>(p, stream);
+        return p.causal ? launch_t<8, 128, true, true>(p, stream) : launch_t<8, 128, false, true>(p, stream);
+    }
     if (p.d == 64) return p.causal ? launch_t<8, 64, true, false>(p, stream) : launch_t<8, 64, false, false>(p, stream);
     return p.causal ? launch_t<8, 128, true, false>(p, stream) : launch_t<8, 128, false, false>(p, stream);
 }

@@ -24,6 +24,7 @@ struct AttnProblem {
     float c;                 // |scale| * log2(e): scores are kept in base-2 units
     bool negate_q;           // scale < 0: q's sign is flipped on load so c >= 0
     bool causal;
+    bool out_f32;            // bf16 inputs, float32 o: single pass uses the partial-store path on o
     // Split over keys: split s covers tiles [s*tiles_per_split, (s+1)*tiles_per_split)
     // of the kernel's key tile size.  splits == 1 writes o and lse directly.
     int splits;

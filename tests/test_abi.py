@@ -54,6 +54,7 @@ def test_constants_match_header():
     for code, name in osa.ERROR_NAMES.items():
         assert codes[name] == code
     assert codes["ATTN_F32"] == osa.ATTN_F32 and codes["ATTN_BF16"] == osa.ATTN_BF16
+    assert codes["ATTN_BF16_OUT_F32"] == osa.ATTN_BF16_OUT_F32
     assert int(re.search(r"#define ATTN_MAX_SPLITS (\d+)", text).group(1)) == osa.ATTN_MAX_SPLITS
 
 
@@ -77,7 +78,7 @@ def test_attn_validation(L, buf):
     assert call(L, buf, N=-3) == SHAPE
     assert call(L, buf, M=-1) == SHAPE
     assert call(L, buf, M=0) == SHAPE
-    assert call(L, buf, dtype=2) == DTYPE
+    assert call(L, buf, dtype=3) == DTYPE
     assert call(L, buf, dtype=-1) == DTYPE
     for d in (0, 32, 96, 256):
         assert call(L, buf, d=d) == HEADDIM
