@@ -226,18 +226,19 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 
 
     if (ntiles > 0) {
-        // Prologue: K(0), V(0) land; S(0) is computed while K(1) loads.
+        // Prologue: every stage is free, so K(0), V(0) and K(1) load together
+        // (one memory latency); S(0) is computed once they have landed.
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             load(krs, 0, lds_k0, i);
             load(vrs, 0, lds_v0, i);
         }
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) load(krs, min(1, ntiles - 1), lds_k1, i);
         if constexpr (BIAS) {
             if (nw > 0) wt.bias_dma(brs, brow, kb, bregion);
         }
         wait_loads_and_barrier<0>();
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) load(krs, min(1, ntiles - 1), lds_k1, i);
         f32x16 sa[2] = {f32x16{}, f32x16{}}, sb[2];
         // Stages alternate with the parity of j: even j reads K(j+1) from k1
         // and V(j) from v0, and refills k0 and v1.
@@ -287,8 +288,19 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         // no LDS-direct load is in flight past this point.
     }
 
-    wt.template store<SPLIT>(N, o + (size_t)bh * N * D, lse + (size_t)bh * N,
-                             part_o + ((size_t)sp * BH + bh) * N * D, part_lse + ((size_t)sp * BH + bh) * N);
+    if constexpr (SPLIT) {
+        wt.template store<true>(N, o + (size_t)bh * N * D, lse + (size_t)bh * N,
+                                part_o + ((size_t)sp * BH + bh) * N * D, part_lse + ((size_t)sp * BH + bh) * N);
+    } else {
+        // The K/V stages are free once every wave is past its last tile: each
+        // wave stages its 32 output rows in its own 64 * D bytes of them.
+        wait_loads_and_barrier<0>();
+        constexpr int TILE = 64 * D;  // bytes of one wave's 32 x D bf16 rows
+        static_assert(TILE * ((NW + 3) / 4) <= T::BYTES, "staged rows fit the stages");
+        char *stage = (wave & 3) == 0 ? lds_k0 : (wave & 3) == 1 ? lds_k1 : (wave & 3) == 2 ? lds_v0 : lds_v1;
+        wt.store_rows(N, q0 + wave * 32, o + (size_t)bh * N * D, lse + (size_t)bh * N, stage + (wave >> 2) * TILE,
+                      lane);
+    }
 }
 
 #define ATTN_KERNEL_ARGS                                                                                       \

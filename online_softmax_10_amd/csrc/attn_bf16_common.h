@@ -318,6 +318,38 @@ struct WaveTile {
         return alpha;
     }
 
+    // Final o = o~ / l (bf16) and LSE, with the rows staged in LDS so each
+    // store instruction writes whole rows: region holds this wave's 32 x D
+    // bf16 tile (16-byte chunk c of row r at chunk c ^ (r % CPR), conflict-
+    // free for the writes and the reads); lane t then stores chunk t % CPR of
+    // row t / CPR + ROWS*i.  The caller makes sure no wave still reads the
+    // region.
+    __device__ __forceinline__ void store_rows(int N, int q_wave, uint16_t *o_head, float *lse_head, char *region,
+                                               int lane) {
+        constexpr int CPR = D / 8;      // 16-byte chunks per row
+        constexpr int ROWS = 64 / CPR;  // rows per store instruction
+        const float l_tot = xhalf_sum(l_run);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (qrow < N && hh == 0) lse_head[qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2 : NEG_INF;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
+                           oacc[db][4 * g + 3] * inv};
+                const int chunk = (4 * db + g) ^ (l32 % CPR);
+                *reinterpret_cast<bf16x4 *>(region + l32 * (2 * D) + chunk * 16 + 8 * hh) = __builtin_convertvector(x, bf16x4);
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
+        const int c = lane % CPR;
+#pragma unroll
+        for (int i = 0; i < 32 / ROWS; ++i) {
+            const int r = lane / CPR + ROWS * i;
+            const u32x4 val = *reinterpret_cast<const u32x4 *>(region + r * (2 * D) + ((c ^ (r % CPR)) * 16));
+            if (q_wave + r < N) *reinterpret_cast<u32x4 *>(o_head + (size_t)(q_wave + r) * D + 8 * c) = val;
+        }
+    }
+
     // Final o = o~ / l and LSE; bf16 output or fp32 split partial.
     template <bool SPLIT>
     __device__ __forceinline__ void store(int N, uint16_t *o_head, float *lse_head, float *part_o_rows,
