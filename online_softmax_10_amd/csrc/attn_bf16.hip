@@ -322,11 +322,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_w8_kernel(ATTN_KERNEL_AR
 }
 
 // Both widths with an additive score bias (staged through 8 KiB of LDS per
-// wave: at d = 128 the four-wave width then fits one workgroup per CU).
+// wave: at d = 128 the four-wave width then needs 96 KiB, one workgroup per CU).
 #define ATTN_BIAS_ARGS \
     ATTN_KERNEL_ARGS, const float *__restrict__ bias, uint32_t bias_bytes, int64_t bias_sb, int64_t bias_sh, int64_t bias_sn
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_bias_kernel(ATTN_BIAS_ARGS) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void attn_fwd_bf16_bias_kernel(ATTN_BIAS_ARGS) {
     attn_body<4, D, CAUSAL, SPLIT, true>(ATTN_KERNEL_PASS, bias, bias_bytes, bias_sb, bias_sh, bias_sn);
 }
 
