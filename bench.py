@@ -77,15 +77,16 @@ def load_traffic(workload: str, kernel: str, path: str = ""):
 COPY_MIB = 512  # size of the plain copy that calibrates the byte counters
 
 
-def counter_commands(wl: str) -> list:
-    """The four rocprofv3 counter runs (from the repository root) that
-    --traffic-from-counters reads back."""
+def counter_commands(wl: str, out_dir: str) -> list:
+    """The four rocprofv3 counter runs (from the repository root, results
+    under out_dir) that --traffic-from-counters reads back."""
     run = f"python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline"
     cal = f"python3 bench.py --calibrate-copy {COPY_MIB} --steps 3"
-    return [f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_{wl} -o run -- {run}",
-            f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_{wl} -o run -- {run}",
-            f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch_copy -o run -- {cal}",
-            f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write_copy -o run -- {cal}"]
+    pmc = "timeout -s KILL 120 rocprofv3 --pmc"
+    return [f"{pmc} FETCH_SIZE --output-format csv -d {out_dir}/pmc_fetch_{wl} -o run -- {run}",
+            f"{pmc} WRITE_SIZE --output-format csv -d {out_dir}/pmc_write_{wl} -o run -- {run}",
+            f"{pmc} FETCH_SIZE --output-format csv -d {out_dir}/pmc_fetch_copy -o run -- {cal}",
+            f"{pmc} WRITE_SIZE --output-format csv -d {out_dir}/pmc_write_copy -o run -- {cal}"]
 
 
 def traffic_from_counters(wl: str, kernel: str, out_dir: str, dest: str = "") -> dict:
@@ -127,7 +128,7 @@ def traffic_from_counters(wl: str, kernel: str, out_dir: str, dest: str = "") ->
         "write_kib_per_dispatch": round(wk, 1),
         "copy_calibration": {"bytes": copy_kib * 1024, "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
         "hbm_bytes_per_launch": round((fk * ff + wk * fw) * 1024),
-        "commands": counter_commands(wl) + [f"python3 bench.py --workload {wl} --traffic-from-counters gpurun_out"],
+        "commands": counter_commands(wl, out_dir) + [f"python3 bench.py --workload {wl} --traffic-from-counters {out_dir}"],
         "note": "KiB per dispatch averaged over the timed dispatches (first excluded); factors = copied bytes / "
                 "counter bytes for a plain device copy",
     }
