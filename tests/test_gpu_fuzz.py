@@ -66,3 +66,22 @@ def test_random_problem(case):
             s = s + np.broadcast_to(bias.astype(np.float64), s.shape)
         logit_max = float(np.max(np.abs(s[np.isfinite(s)]))) if np.isfinite(s).any() else 8.0
         compare(o[vis], lse[vis], o_ref[vis], lse_ref[vis], w.dtype, f"fuzz {case}", logit_max=max(8.0, logit_max))
+
+
+@pytest.mark.parametrize("N,M,causal,dtype", [(1, 300001, False, "bf16"), (5, 262147, "bottom_right", "bf16"),
+                                              (130, 200003, False, "bf16"), (3, 100003, "bottom_right", "f32")])
+def test_long_key_range(N, M, causal, dtype):
+    # Key ranges long enough for the split planner's upper end and long sums.
+    import torch
+
+    import online_softmax_10_amd as osa
+
+    w = si.Workload("long", 1, 2, N, M, 128, dtype, causal is not False, "normal")
+    log(f"[gpu] long keys N={N} M={M} causal={causal} {dtype} plan={osa.plan(1, 2, N, M, 128, dtype)}")
+    q, k, v = si.make_qkv(w, 77)
+    qd, kd, vd = (to_device(a, dtype) for a in (q, k, v))
+    o, lse = osa.fwd(qd, kd, vd, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(si.to_f64(q, dtype), si.to_f64(k, dtype), si.to_f64(v, dtype), w.scale, causal)
+    compare(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, dtype,
+            f"long keys M={M}")
