@@ -227,18 +227,21 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 
     if (ntiles > 0) {
         // Prologue: every stage is free, so K(0), V(0) and K(1) load together
-        // (one memory latency); S(0) is computed once they have landed.
+        // (one memory latency).  S(0) needs only Q and K(0) (and tile 0's
+        // bias), issued first: it is computed once they have landed, while
+        // V(0) and K(1) -- the last 2 * LOADS loads of each wave -- may still
+        // be on their way (the first iteration waits for them).
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            load(krs, 0, lds_k0, i);
-            load(vrs, 0, lds_v0, i);
-        }
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) load(krs, min(1, ntiles - 1), lds_k1, i);
+        for (int i = 0; i < LOADS; ++i) load(krs, 0, lds_k0, i);
         if constexpr (BIAS) {
             if (nw > 0) wt.bias_dma(brs, brow, kb, bregion);
         }
-        wait_loads_and_barrier<0>();
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            load(vrs, 0, lds_v0, i);
+            load(krs, min(1, ntiles - 1), lds_k1, i);
+        }
+        wait_loads_and_barrier<2 * LOADS>();
         f32x16 sa[2] = {f32x16{}, f32x16{}}, sb[2];
         // Stages alternate with the parity of j: even j reads K(j+1) from k1
         // and V(j) from v0, and refills k0 and v1.

@@ -210,13 +210,16 @@ struct WaveTile {
         // Accumulator register r of block cb holds key kv0 + 32*cb + 16*(r/8) + 8*hh + r%8.
         const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > wq_lo + coff);
         if (need_mask) {
+            // Key kv0 + 8*hh + off is visible iff off <= lim (key < ke, and
+            // key <= qrow + coff when causal): one compare with a constant per score.
+            int lim = ke - 1 - kv0 - 8 * hh;
+            if (CAUSAL) lim = min(lim, qrow + coff - kv0 - 8 * hh);
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + 32 * cb + 16 * (r >> 3) + 8 * hh + (r & 7);
-                    const bool ok = key < ke && (!CAUSAL || key <= qrow + coff);
-                    s[cb][r] = ok ? s[cb][r] : NEG_INF;
+                    const int off = 32 * cb + 16 * (r >> 3) + (r & 7);
+                    s[cb][r] = off <= lim ? s[cb][r] : NEG_INF;
                 }
         }
     }
