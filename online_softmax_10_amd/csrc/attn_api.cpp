@@ -35,7 +35,16 @@ struct Plan {
 
 // Work decomposition.  num_splits: 0 = choose, 1 = single pass, >= 2 = split.
 // Calls with a bias never take the decode kernel.
-Plan plan_for(int64_t BH, int64_t N, int64_t M, bool bf16, int num_splits, bool bias = false) {
+// A split costs a workspace, the merge kernel and their host calls -- about
+// 15-20 us per call on MI355X against a single pass of the same small
+// problem.  It pays only when a workgroup's key loop is long: measured on
+// twelve shapes (256-8192 queries, 256-16384 keys, d = 64 and 128, causal or
+// not) the single pass won below 64 units of work per query tile and the split
+// above 128, a unit being 64 keys at d = 64 in bf16; the fp32 kernel (matrix
+// rate 1/16 of bf16) counts 32 units per bf16 unit.
+constexpr int64_t kMinSplitUnits = 96;
+
+Plan plan_for(int64_t BH, int64_t N, int64_t M, int d, bool bf16, int num_splits, bool bias = false) {
     const bool few_queries = N <= osa::kDecodeMaxQueries && !bias;
     if (num_splits == 1) return Plan{Plan::SINGLE, 1, 0};
     if (few_queries) {
@@ -61,6 +70,8 @@ Plan plan_for(int64_t BH, int64_t N, int64_t M, bool bf16, int num_splits, bool 
         // units and the key range is long enough to share out.
         const int64_t wgs = BH * row_tiles;
         if (wgs >= 256) return Plan{Plan::SINGLE, 1, 0};
+        const int64_t units = ((M + 63) / 64) * (d / 64) * (bf16 ? 1 : 32);
+        if (units < kMinSplitUnits) return Plan{Plan::SINGLE, 1, 0};
         s = ceil_div(512, wgs);
         const int cap = ceil_div(M, 4 * tile);
         if (s > cap) s = cap;
@@ -167,7 +178,7 @@ int run_attn(const void *q, const void *k, const void *v, void *o, float *lse, i
     p.causal = causal != ATTN_CAUSAL_NONE;
     p.out_f32 = dtype == ATTN_BF16_OUT_F32;
 
-    const Plan plan = plan_for(BH, N, M, bf16, num_splits, p.bias != nullptr);
+    const Plan plan = plan_for(BH, N, M, d, bf16, num_splits, p.bias != nullptr);
     const int64_t blocks = plan.kind == Plan::DECODE ? BH * plan.splits : BH * ceil_div(N, 128) * plan.splits;
     if (blocks > kMaxBlocks) return ATTN_ERR_OVERFLOW;
     const MainKernel kernel = main_kernel(plan, BH, N, bf16, p.bias != nullptr, p.out_f32);
@@ -337,7 +348,7 @@ const char *attn_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int d, int
     if (num_splits < 0 || num_splits > ATTN_MAX_SPLITS) return nullptr;
     if (B > kI32Max || H > kI32Max || B * H > kI32Max || N > kI32Max / d || M > kI32Max / d) return nullptr;
     const bool bf16 = dtype != ATTN_F32;
-    const Plan plan = plan_for(B * H, N, M, bf16, num_splits);
+    const Plan plan = plan_for(B * H, N, M, d, bf16, num_splits);
     if (splits) *splits = plan.splits;
     return main_kernel_name(main_kernel(plan, B * H, N, bf16));
 }

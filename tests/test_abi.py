@@ -153,8 +153,16 @@ def test_plan_kernel_choice():
     assert name == "attn_decode_kernel" and 1 <= s <= osa.ATTN_MAX_SPLITS
     assert osa.plan(1, 1, 256, 256, 64, "f32")[0] == "attn_fwd_f32_kernel"
     # Few query tiles and a long key range: split partials, merged afterwards.
-    name, s = osa.plan(1, 1, 100, 5000, 64)
+    name, s = osa.plan(1, 1, 100, 8000, 64)
     assert name == "attn_fwd_bf16_kernel" and s > 1
+    name, s = osa.plan(1, 1, 4096, 4096, 128)
+    assert name == "attn_fwd_bf16_kernel" and s > 1
+    # Few query tiles but a short key loop: the split's workspace, merge kernel
+    # and host calls would cost more than they save.
+    assert osa.plan(2, 4, 512, 512, 64) == ("attn_fwd_bf16_kernel", 1)
+    assert osa.plan(1, 16, 1024, 1024, 128) == ("attn_fwd_bf16_kernel", 1)
+    assert osa.plan(1, 2, 2048, 2048, 64) == ("attn_fwd_bf16_kernel", 1)
+    assert osa.plan(1, 1, 256, 256, 64, "f32")[1] > 1
     # An explicit single pass on a small problem takes the four-wave kernel;
     # the eight-wave kernel never writes partials.
     assert osa.plan(1, 1, 100, 5000, 64, num_splits=1) == ("attn_fwd_bf16_kernel", 1)
