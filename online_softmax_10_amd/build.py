@@ -31,6 +31,10 @@ FLAGS = [
     "-Wall",
     # Keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Kernel arguments arrive preloaded in SGPRs: a workgroup's first address
+    # computations need not wait for a scalar load of the argument block
+    # (attention: -0.3 % per launch on 2x16x4096^2 causal, -1 % on 4x8x1024^2).
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", INCLUDE,
 ]
 
