@@ -66,6 +66,11 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     constexpr int PSLOTS = 4 * (D / 32);  // P.V MFMAs per tile
     constexpr int EVERY = SLOTS / LOADS;  // score slots per load pair
     static_assert(LOADS * NW == T::LOADS && LOADS >= 1 && EVERY >= 1, "tile split");
+    // Scores shifted during the previous P.V phase (d = 128 without a bias).
+    // At d = 64 the 8 P.V MFMAs of a tile hide the shift less well than the
+    // score phase does (4x8x1024^2: +3.8 % per launch), and the bias path
+    // adds the bias there.
+    constexpr bool XS = !BIAS && D == 128;
     __shared__ __attribute__((aligned(1024))) char lds_k0[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_k1[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_v0[T::BYTES];
@@ -129,12 +134,16 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     // with.  Load tile indices past the last are clamped to it: a harmless
     // reload into a free stage that keeps the block free of branches.
     // bias_next: this wave computes tile j+2 too (its bias is fetched here).
+    // XS: s_cur arrives masked and shifted (x = c*s - sh, sh the shift base
+    // when it was shifted): the P.V phase of the previous iteration (the
+    // prologue for tile 0) did both while its MFMAs ran, and this iteration
+    // does the same for s_nxt.
     auto iteration = [&](auto full, auto loads, int j, bool bias_next, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                          const char *ks_next, char *ks_free, const char *vs_cur, char *vs_free) {
         constexpr bool FULL = decltype(full)::value;
         constexpr bool LOADS_ON = decltype(loads)::value;
         wait_loads_and_barrier<0>();
-        wt.mask(kb + j * BC, ke, s_cur);  // s_cur holds the bias already (added during the last P.V phase)
+        if constexpr (!XS) wt.mask(kb + j * BC, ke, s_cur);  // with a bias, s_cur holds it already (added during the last P.V phase)
         const float m = wt.m_run;
         uint32_t popw[BC / 16][4];
         float lsum0 = 0.f, lsum1 = 0.f;
@@ -157,7 +166,8 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 #pragma unroll
             for (int u = 0; u < 32 / SLOTS; u += 2) {
                 const int e = slot * (32 / SLOTS) + u;
-                wt.prob_pair(s_cur, e, m, popw, (e & 2) ? lsum1 : lsum0);
+                if constexpr (XS) wt.prob_pair_x(s_cur, e, popw, (e & 2) ? lsum1 : lsum0);
+                else wt.prob_pair(s_cur, e, m, popw, (e & 2) ? lsum1 : lsum0);
             }
             if constexpr (LOADS_ON) {
                 if (slot % EVERY == EVERY - 1) {
@@ -172,10 +182,16 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         for (int g = 0; g < BC / 16; ++g)
             pop[g] = __builtin_bit_cast(bf16x8, (u32x4{popw[g][0], popw[g][1], popw[g][2], popw[g][3]}));
         float lsum = lsum0 + lsum1;
-        // Some row's tile sum above the limit, or not finite: the exact path.
+        // Some row's tile sum above the limit, or not finite (or, shifted, a
+        // row's first visible key): the exact path.
         float alpha = 1.f;
-        if (__builtin_amdgcn_ballot_w64(!(lsum <= SHIFT_SUM_LIMIT)) != 0) alpha = wt.exact_shift(s_cur, pop, lsum);
+        if constexpr (XS) {
+            if (__builtin_amdgcn_ballot_w64(wt.needs_exact_x(lsum)) != 0) alpha = wt.exact_shift_x(s_cur, pop, lsum);
+        } else {
+            if (__builtin_amdgcn_ballot_w64(!(lsum <= SHIFT_SUM_LIMIT)) != 0) alpha = wt.exact_shift(s_cur, pop, lsum);
+        }
         wt.l_run = alpha * wt.l_run + lsum;
+        const float sh = wt.shift_base();  // for tile j+1's scores
 
         bf16x8 vop[3];
         vop[0] = wt.vread(vs_cur, 0);
@@ -186,10 +202,16 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             const int t4 = slot / (D / 32), db = slot % (D / 32);
             wt.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[slot % 3], pop[t4], wt.oacc[db], 0, 0, 0);
             if (slot + 2 < PSLOTS) vop[(slot + 2) % 3] = wt.vread(vs_cur, slot + 2);
-            // The VALU is free here: the bias of tile j+1 (staged during the
-            // last iteration, landed with this iteration's wait) goes into its
-            // scores, run by run; then tile j+2's bias is fetched into the
-            // same region, once every read of it has returned.
+            // The VALU is free here.  XS: tile j+1's scores are shifted,
+            // 32 / PSLOTS per slot.  With a bias: the bias of tile
+            // j+1 (staged during the last iteration, landed with this
+            // iteration's wait) goes into its scores, run by run; then tile
+            // j+2's bias is fetched into the same region, once every read of
+            // it has returned.
+            if constexpr (XS && FULL) {
+#pragma unroll
+                for (int u = 0; u < 32 / PSLOTS; u += 2) wt.shift_pair(s_nxt, slot * (32 / PSLOTS) + u, sh);
+            }
             if constexpr (BIAS && FULL) {
                 constexpr int PER = (8 + PSLOTS / 2 - 1) / (PSLOTS / 2);  // runs per slot over the first half
                 if (slot < PSLOTS / 2) {
@@ -203,6 +225,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             }
             fence();
         }
+        if constexpr (XS && FULL) wt.mask(kb + (j + 1) * BC, ke, s_nxt);
     };
     using Full = std::integral_constant<bool, true>;
     using Last = std::integral_constant<bool, false>;
@@ -249,6 +272,12 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         if (nw > 0) {
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) wt.score_step(lds_k0, kk, sa);
+            if constexpr (XS) {
+                // Tile 0 shifted against base 0 (no shift yet) and masked.
+#pragma unroll
+                for (int e = 0; e < 32; e += 2) wt.shift_pair(sa, e, 0.f);
+                wt.mask(kb, ke, sa);
+            }
             if constexpr (BIAS) {
                 // Tile 0's bias landed with the prologue's wait; tile 1's follows.
 #pragma unroll

@@ -256,13 +256,17 @@ struct WaveTile {
     // weights: with a peaked softmax the rounding of the dominant weights
     // cancels.
     __device__ __forceinline__ float probs(const f32x16 (&s)[2], float m, bf16x8 (&pop)[BC / 16]) const {
+        return probs_scaled(s, c, m, pop);
+    }
+    // The same with the scale given: P = 2^(cs*s - m).
+    __device__ __forceinline__ float probs_scaled(const f32x16 (&s)[2], float cs, float m, bf16x8 (&pop)[BC / 16]) const {
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         float lsum[2] = {0.f, 0.f};  // two chains of v_dot2c
 #pragma unroll
         for (int t4 = 0; t4 < BC / 16; ++t4) {
             f32x8 p;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) p[i] = exp2_fast(__builtin_fmaf(s[t4 >> 1][8 * (t4 & 1) + i], c, -m));
+            for (int i = 0; i < 8; ++i) p[i] = exp2_fast(__builtin_fmaf(s[t4 >> 1][8 * (t4 & 1) + i], cs, -m));
             pop[t4] = __builtin_convertvector(p, bf16x8);
             float &acc = lsum[t4 & 1];
             acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop[t4], pop[t4], 0, 1), ones, acc, false);
@@ -299,6 +303,61 @@ struct WaveTile {
         const bf16x2 pp = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
         popw[e >> 3][(e & 7) >> 1] = __builtin_bit_cast(uint32_t, pp);
         acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+    }
+
+    // The shift a tile's scores are taken against before the tile is seen:
+    // the running one, or 0 for a row that has no shift yet (no visible key
+    // so far).
+    __device__ __forceinline__ float shift_base() const { return m_run == NEG_INF ? 0.f : m_run; }
+
+    // Scores e, e+1 (e even) brought to base-2 units against shift sh, in
+    // place: x = c*s - sh.  Done for the next tile while the P.V MFMAs of this
+    // one run, so the score phase is left with the exponentials
+    // (prob_pair_x); a masked -inf stays -inf.
+    __device__ __forceinline__ void shift_pair(f32x16 (&s)[2], int e, float sh) const {
+        s[e >> 4][e & 15] = __builtin_fmaf(s[e >> 4][e & 15], c, -sh);
+        s[(e + 1) >> 4][(e + 1) & 15] = __builtin_fmaf(s[(e + 1) >> 4][(e + 1) & 15], c, -sh);
+    }
+
+    // prob_pair for shifted scores x (shift_pair): P = 2^x.
+    __device__ __forceinline__ void prob_pair_x(const f32x16 (&x)[2], int e, uint32_t (&popw)[BC / 16][4],
+                                                float &acc) const {
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        const float p0 = exp2_fast(x[e >> 4][e & 15]);
+        const float p1 = exp2_fast(x[(e + 1) >> 4][(e + 1) & 15]);
+        const bf16x2 pp = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+        popw[e >> 3][(e & 7) >> 1] = __builtin_bit_cast(uint32_t, pp);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+    }
+
+    // Whether this lane's row needs the exact path for a tile of shifted
+    // scores with probability sum lsum: the sum is above the limit or not
+    // finite, or the row has no shift yet (its first tile: scores far below
+    // the base 0 would otherwise underflow to a zero sum).
+    __device__ __forceinline__ bool needs_exact_x(float lsum) const {
+        return !(lsum <= SHIFT_SUM_LIMIT) || m_run == NEG_INF;
+    }
+
+    // Exact path for shifted scores x = c*s - sh (sh = shift_base()): the row
+    // max of c*s is sh + max x; the shift becomes the larger of that and the
+    // running one, and P = 2^(x - (m_new - sh)).  A row with no visible key
+    // in this tile keeps its shift (and, with none so far, its zero state).
+    __device__ __forceinline__ float exact_shift_x(const f32x16 (&x)[2], bf16x8 (&pop)[BC / 16], float &lsum) {
+        float mx = NEG_INF;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[cb][r]);
+        mx = xhalf_max(mx);
+        const float sh = shift_base();
+        const float m_new = mx == NEG_INF ? m_run : fmaxf(m_run, sh + mx);
+        const float delta = mx == NEG_INF ? 0.f : m_new - sh;
+        const float alpha = m_new == NEG_INF ? 1.f : exp2_fast(m_run - m_new);  // 0 when m_run was -inf
+        m_run = m_new;
+        lsum = probs_scaled(x, 1.f, delta, pop);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        return alpha;
     }
 
     // Exact path of one tile: row max, new shift, rescale of o~ (l is rescaled

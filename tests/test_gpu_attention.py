@@ -139,6 +139,23 @@ def test_c4_stress_constant_v():
             "c4-like V=1")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_scores_far_below_zero(d, causal, splits):
+    # Every scaled score near -300 (about -430 in base 2), a few units apart:
+    # against a zero shift a row's first tile sums to 0 in fp32, so the kernel
+    # must still set the row's shift from that tile (and, split over keys,
+    # from the first tile of each range that holds a visible key).
+    w = si.Workload("negscores", 1, 2, 300, 333, d, "bf16", causal, "normal")
+    rng = np.random.default_rng(11)
+    a = np.sqrt(300.0 / (d * float(w.scale)))  # q ~ a + noise, k ~ -a + noise: scale * q.k ~ -300
+    q = (a + 0.3 * rng.standard_normal((w.B, w.H, w.N, d))).astype(np.float32)
+    k = (-a + 0.3 * rng.standard_normal((w.B, w.H, w.M, d))).astype(np.float32)
+    v = rng.standard_normal((w.B, w.H, w.M, d)).astype(np.float32)
+    check_full(w, 11, splits=splits, qkv=tuple(si.f32_to_bf16_bits(x) for x in (q, k, v)))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_query_uniform(dtype):
     w = si.Workload("zeroq", 1, 2, 160, 300, 64, dtype, True, "normal")
