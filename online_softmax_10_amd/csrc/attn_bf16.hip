@@ -71,6 +71,12 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     // score phase does (4x8x1024^2: +3.8 % per launch), and the bias path
     // adds the bias there.
     constexpr bool XS = !BIAS && D == 128;
+    // XS: probability pairs of the next tile formed during the P.V phase
+    // (the rest in the score phase); their packed values and sum carry over.
+    // 4 of the 16 (paired A/B: c3 -1.4 %, c4 -0.3 %; 8 pairs gained nothing).
+    constexpr int EARLY = 4;
+    uint32_t popw[BC / 16][4];
+    float lsum_early = 0.f;
     __shared__ __attribute__((aligned(1024))) char lds_k0[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_k1[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_v0[T::BYTES];
@@ -145,7 +151,6 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         wait_loads_and_barrier<0>();
         if constexpr (!XS) wt.mask(kb + j * BC, ke, s_cur);  // with a bias, s_cur holds it already (added during the last P.V phase)
         const float m = wt.m_run;
-        uint32_t popw[BC / 16][4];
         float lsum0 = 0.f, lsum1 = 0.f;
         bf16x8 kop[3];
         if constexpr (FULL) {
@@ -163,11 +168,18 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
                 if (slot + 2 < SLOTS) kop[(slot + 2) % 3] = wt.kread(ks_next, slot + 2);
             }
             // 32 scores over SLOTS slots: two per slot at d = 128, four at d = 64.
+            if constexpr (XS) {
+                // the pairs left after the early ones, spread over the slots
+                constexpr int LEFT = 16 - EARLY;
 #pragma unroll
-            for (int u = 0; u < 32 / SLOTS; u += 2) {
-                const int e = slot * (32 / SLOTS) + u;
-                if constexpr (XS) wt.prob_pair_x(s_cur, e, popw, (e & 2) ? lsum1 : lsum0);
-                else wt.prob_pair(s_cur, e, m, popw, (e & 2) ? lsum1 : lsum0);
+                for (int pp = EARLY + (slot * LEFT) / SLOTS; pp < EARLY + ((slot + 1) * LEFT) / SLOTS; ++pp)
+                    wt.prob_pair_x(s_cur, 2 * pp, popw, (pp & 1) ? lsum1 : lsum0);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 32 / SLOTS; u += 2) {
+                    const int e = slot * (32 / SLOTS) + u;
+                    wt.prob_pair(s_cur, e, m, popw, (e & 2) ? lsum1 : lsum0);
+                }
             }
             if constexpr (LOADS_ON) {
                 if (slot % EVERY == EVERY - 1) {
@@ -182,6 +194,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         for (int g = 0; g < BC / 16; ++g)
             pop[g] = __builtin_bit_cast(bf16x8, (u32x4{popw[g][0], popw[g][1], popw[g][2], popw[g][3]}));
         float lsum = lsum0 + lsum1;
+        if constexpr (XS) lsum += lsum_early;
         // Some row's tile sum above the limit, or not finite (or, shifted, a
         // row's first visible key): the exact path.
         float alpha = 1.f;
@@ -196,6 +209,10 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         bf16x8 vop[3];
         vop[0] = wt.vread(vs_cur, 0);
         vop[1] = wt.vread(vs_cur, 1);
+        // XS: the next tile's scores are masked first (its early pairs are
+        // formed below); a masked -inf stays -inf when shifted.
+        if constexpr (XS && FULL) wt.mask(kb + (j + 1) * BC, ke, s_nxt);
+        float le0 = 0.f, le1 = 0.f;
         fence();
 #pragma unroll
         for (int slot = 0; slot < PSLOTS; ++slot) {
@@ -211,6 +228,8 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             if constexpr (XS && FULL) {
 #pragma unroll
                 for (int u = 0; u < 32 / PSLOTS; u += 2) wt.shift_pair(s_nxt, slot * (32 / PSLOTS) + u, sh);
+                // early pair slot-1 (shifted in the previous slot)
+                if (slot >= 1 && slot - 1 < EARLY) wt.prob_pair_x(s_nxt, 2 * (slot - 1), popw, ((slot - 1) & 1) ? le1 : le0);
             }
             if constexpr (BIAS && FULL) {
                 constexpr int PER = (8 + PSLOTS / 2 - 1) / (PSLOTS / 2);  // runs per slot over the first half
@@ -225,7 +244,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             }
             fence();
         }
-        if constexpr (XS && FULL) wt.mask(kb + (j + 1) * BC, ke, s_nxt);
+        if constexpr (XS && FULL) lsum_early = le0 + le1;
     };
     using Full = std::integral_constant<bool, true>;
     using Last = std::integral_constant<bool, false>;
@@ -273,10 +292,15 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) wt.score_step(lds_k0, kk, sa);
             if constexpr (XS) {
-                // Tile 0 shifted against base 0 (no shift yet) and masked.
+                // Tile 0 masked, shifted against base 0 (no shift yet), its
+                // early pairs formed.
+                wt.mask(kb, ke, sa);
 #pragma unroll
                 for (int e = 0; e < 32; e += 2) wt.shift_pair(sa, e, 0.f);
-                wt.mask(kb, ke, sa);
+                float le = 0.f;
+#pragma unroll
+                for (int e = 0; e < 2 * EARLY; e += 2) wt.prob_pair_x(sa, e, popw, le);
+                lsum_early = le;
             }
             if constexpr (BIAS) {
                 // Tile 0's bias landed with the prologue's wait; tile 1's follows.
