@@ -66,11 +66,11 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     constexpr int PSLOTS = 4 * (D / 32);  // P.V MFMAs per tile
     constexpr int EVERY = SLOTS / LOADS;  // score slots per load pair
     static_assert(LOADS * NW == T::LOADS && LOADS >= 1 && EVERY >= 1, "tile split");
-    // Scores shifted during the previous P.V phase (d = 128 without a bias).
-    // At d = 64 the 8 P.V MFMAs of a tile hide the shift less well than the
-    // score phase does (4x8x1024^2: +3.8 % per launch), and the bias path
-    // adds the bias there.
-    constexpr bool XS = !BIAS && D == 128;
+    // Scores shifted during the previous P.V phase (without a bias: the bias
+    // path adds the bias there).  Paired A/B per launch: 2x16x4096^2 causal
+    // -3.8 % at d = 128 (-6.7 % at d = 64), 1x8x16384^2 causal -2.5 %;
+    // 4x8x1024^2 at d = 64, one wave per SIMD, unchanged.
+    constexpr bool XS = !BIAS;
     // XS: probability pairs of the next tile formed during the P.V phase
     // (the rest in the score phase); their packed values and sum carry over.
     // 4 of the 16 (paired A/B: c3 -1.4 %, c4 -0.3 %; 8 pairs gained nothing).
