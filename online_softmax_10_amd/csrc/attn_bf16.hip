@@ -66,15 +66,19 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     constexpr int PSLOTS = 4 * (D / 32);  // P.V MFMAs per tile
     constexpr int EVERY = SLOTS / LOADS;  // score slots per load pair
     static_assert(LOADS * NW == T::LOADS && LOADS >= 1 && EVERY >= 1, "tile split");
-    // Scores shifted during the previous P.V phase (without a bias: the bias
-    // path adds the bias there).  Paired A/B per launch: 2x16x4096^2 causal
-    // -3.8 % at d = 128 (-6.7 % at d = 64), 1x8x16384^2 causal -2.5 %;
-    // 4x8x1024^2 at d = 64, one wave per SIMD, unchanged.
-    constexpr bool XS = !BIAS;
+    // Scores shifted during the previous P.V phase (with a bias, by the FMA
+    // that adds it).  Paired A/B per launch: 2x16x4096^2 causal -3.8 % at
+    // d = 128 (-6.7 % at d = 64), 1x8x16384^2 causal -2.5 %; 4x8x1024^2 at
+    // d = 64, one wave per SIMD, unchanged; with an [N, M] bias -2.4 % to
+    // -2.7 % at d = 64, but +7.4 % at d = 128, where the bias kernel then
+    // spills in its key loop -- so not there.
+    constexpr bool XS = !BIAS || D == 64;
     // XS: probability pairs of the next tile formed during the P.V phase
     // (the rest in the score phase); their packed values and sum carry over.
-    // 4 of the 16 (paired A/B: c3 -1.4 %, c4 -0.3 %; 8 pairs gained nothing).
-    constexpr int EARLY = 4;
+    // 4 of the 16 (paired A/B: c3 -1.4 %, c4 -0.3 %; 8 pairs gained nothing);
+    // none with a bias, whose runs are added during the first half of the
+    // P.V phase.
+    constexpr int EARLY = BIAS ? 0 : 4;
     uint32_t popw[BC / 16][4];
     float lsum_early = 0.f;
     __shared__ __attribute__((aligned(1024))) char lds_k0[T::BYTES];
@@ -225,7 +229,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             // iteration's wait) goes into its scores, run by run; then tile
             // j+2's bias is fetched into the same region, once every read of
             // it has returned.
-            if constexpr (XS && FULL) {
+            if constexpr (XS && FULL && !BIAS) {
 #pragma unroll
                 for (int u = 0; u < 32 / PSLOTS; u += 2) wt.shift_pair(s_nxt, slot * (32 / PSLOTS) + u, sh);
                 // early pair slot-1 (shifted in the previous slot)
@@ -235,7 +239,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
                 constexpr int PER = (8 + PSLOTS / 2 - 1) / (PSLOTS / 2);  // runs per slot over the first half
                 if (slot < PSLOTS / 2) {
 #pragma unroll
-                    for (int t = slot * PER; t < slot * PER + PER && t < 8; ++t) wt.bias_apply(bregion, t, lane, s_nxt, c);
+                    for (int t = slot * PER; t < slot * PER + PER && t < 8; ++t) wt.bias_apply(bregion, t, lane, s_nxt, c, XS ? sh : 0.f);
                 }
                 if (slot == PSLOTS / 2 && bias_next) {
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -292,20 +296,30 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) wt.score_step(lds_k0, kk, sa);
             if constexpr (XS) {
-                // Tile 0 masked, shifted against base 0 (no shift yet), its
-                // early pairs formed.
+                // Tile 0 masked, shifted against base 0 (no shift yet) -- with
+                // a bias by adding it (landed with the prologue's wait) --,
+                // its early pairs formed.
                 wt.mask(kb, ke, sa);
+                if constexpr (BIAS) {
 #pragma unroll
-                for (int e = 0; e < 32; e += 2) wt.shift_pair(sa, e, 0.f);
+                    for (int t = 0; t < 8; ++t) wt.bias_apply(bregion, t, lane, sa, c, 0.f);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 32; e += 2) wt.shift_pair(sa, e, 0.f);
+                }
                 float le = 0.f;
 #pragma unroll
                 for (int e = 0; e < 2 * EARLY; e += 2) wt.prob_pair_x(sa, e, popw, le);
                 lsum_early = le;
             }
-            if constexpr (BIAS) {
-                // Tile 0's bias landed with the prologue's wait; tile 1's follows.
+            if constexpr (!XS && BIAS) {
+                // Tile 0's bias landed with the prologue's wait (the mask
+                // follows at the start of the first iteration).
 #pragma unroll
-                for (int t = 0; t < 8; ++t) wt.bias_apply(bregion, t, lane, sa, c);
+                for (int t = 0; t < 8; ++t) wt.bias_apply(bregion, t, lane, sa, c, 0.f);
+            }
+            if constexpr (BIAS) {
+                // Tile 1's bias follows tile 0's.
                 if (nw > 1) {
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                     wt.bias_dma(brs, brow, kb + BC, bregion);

@@ -239,15 +239,14 @@ struct WaveTile {
         }
     }
 
-    // Run t of the staged bias into s: s <- c_scale * s + log2(e) * bias, the
-    // scores in base-2 units with the bias added (the tile math then runs
-    // with c = 1).
+    // Run t of the staged bias into s: s <- c_scale * s + log2(e) * bias - sh,
+    // the scores in base-2 units with the bias added, against shift sh.
     __device__ __forceinline__ void bias_apply(const char *region, int t, int lane, f32x16 (&s)[2],
-                                               float c_scale) const {
+                                               float c_scale, float sh) const {
         const f32x4 b = *reinterpret_cast<const f32x4 *>(region + 1024 * t + 16 * lane);
         const int cb = t >> 2, r0 = 8 * ((t >> 1) & 1) + 4 * (t & 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[cb][r0 + e] = __builtin_fmaf(s[cb][r0 + e], c_scale, b[e] * LOG2E);
+        for (int e = 0; e < 4; ++e) s[cb][r0 + e] = __builtin_fmaf(s[cb][r0 + e], c_scale, __builtin_fmaf(b[e], LOG2E, -sh));
     }
 
     // P = 2^(c*s - m) for shift m, rounded to bf16 as the operands of P.V;
