@@ -66,14 +66,16 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     constexpr int PSLOTS = 4 * (D / 32);  // P.V MFMAs per tile
     constexpr int EVERY = SLOTS / LOADS;  // score slots per load pair
     static_assert(LOADS * NW == T::LOADS && LOADS >= 1 && EVERY >= 1, "tile split");
-    // Scores shifted during the previous P.V phase (with a bias, by the FMA
-    // that adds it).  Paired A/B per launch: 2x16x4096^2 causal -3.8 % at
-    // d = 128 (-6.7 % at d = 64), 1x8x16384^2 causal -2.5 %; 4x8x1024^2 at
-    // d = 64, one wave per SIMD, unchanged; with an [N, M] bias -2.4 % to
-    // -2.7 % at d = 64, but +7.4 % at d = 128, where the bias kernel then
-    // spills in its key loop -- so not there.
-    constexpr bool XS = !BIAS || D == 64;
-    // XS: probability pairs of the next tile formed during the P.V phase
+    // Scores arrive shifted: the previous P.V phase brought them to base-2
+    // units against the shift (with a bias, in the FMA that adds it).  Paired
+    // A/B per launch against shifting in the score phase: 2x16x4096^2 causal
+    // -3.8 % at d = 128 (-6.7 % at d = 64), 1x8x16384^2 causal -2.5 %;
+    // 4x8x1024^2 at d = 64, one wave per SIMD, unchanged; with an [N, M]
+    // bias -2.5 % at d = 64 and -1.5 % at d = 128.  MASK_LATE: with a bias
+    // at d = 128 the mask is applied at the start of the iteration (masking
+    // during the P.V phase made that kernel spill in its key loop, +7.4 %).
+    constexpr bool MASK_LATE = BIAS && D == 128;
+    // Probability pairs of the next tile formed during the P.V phase
     // (the rest in the score phase); their packed values and sum carry over.
     // 4 of the 16 (paired A/B: c3 -1.4 %, c4 -0.3 %; 8 pairs gained nothing);
     // none with a bias, whose runs are added during the first half of the
@@ -144,17 +146,16 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     // with.  Load tile indices past the last are clamped to it: a harmless
     // reload into a free stage that keeps the block free of branches.
     // bias_next: this wave computes tile j+2 too (its bias is fetched here).
-    // XS: s_cur arrives masked and shifted (x = c*s - sh, sh the shift base
-    // when it was shifted): the P.V phase of the previous iteration (the
-    // prologue for tile 0) did both while its MFMAs ran, and this iteration
-    // does the same for s_nxt.
+    // s_cur arrives shifted (x = c*s - sh, sh the shift base when it was
+    // shifted) and, unless MASK_LATE, masked: the P.V phase of the previous
+    // iteration (the prologue for tile 0) did both while its MFMAs ran, and
+    // this iteration does the same for s_nxt.
     auto iteration = [&](auto full, auto loads, int j, bool bias_next, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                          const char *ks_next, char *ks_free, const char *vs_cur, char *vs_free) {
         constexpr bool FULL = decltype(full)::value;
         constexpr bool LOADS_ON = decltype(loads)::value;
         wait_loads_and_barrier<0>();
-        if constexpr (!XS) wt.mask(kb + j * BC, ke, s_cur);  // with a bias, s_cur holds it already (added during the last P.V phase)
-        const float m = wt.m_run;
+        if constexpr (MASK_LATE) wt.mask(kb + j * BC, ke, s_cur);
         float lsum0 = 0.f, lsum1 = 0.f;
         bf16x8 kop[3];
         if constexpr (FULL) {
@@ -172,18 +173,12 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
                 if (slot + 2 < SLOTS) kop[(slot + 2) % 3] = wt.kread(ks_next, slot + 2);
             }
             // 32 scores over SLOTS slots: two per slot at d = 128, four at d = 64.
-            if constexpr (XS) {
+            {
                 // the pairs left after the early ones, spread over the slots
                 constexpr int LEFT = 16 - EARLY;
 #pragma unroll
                 for (int pp = EARLY + (slot * LEFT) / SLOTS; pp < EARLY + ((slot + 1) * LEFT) / SLOTS; ++pp)
                     wt.prob_pair_x(s_cur, 2 * pp, popw, (pp & 1) ? lsum1 : lsum0);
-            } else {
-#pragma unroll
-                for (int u = 0; u < 32 / SLOTS; u += 2) {
-                    const int e = slot * (32 / SLOTS) + u;
-                    wt.prob_pair(s_cur, e, m, popw, (e & 2) ? lsum1 : lsum0);
-                }
             }
             if constexpr (LOADS_ON) {
                 if (slot % EVERY == EVERY - 1) {
@@ -197,25 +192,20 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 #pragma unroll
         for (int g = 0; g < BC / 16; ++g)
             pop[g] = __builtin_bit_cast(bf16x8, (u32x4{popw[g][0], popw[g][1], popw[g][2], popw[g][3]}));
-        float lsum = lsum0 + lsum1;
-        if constexpr (XS) lsum += lsum_early;
-        // Some row's tile sum above the limit, or not finite (or, shifted, a
-        // row's first visible key): the exact path.
+        float lsum = lsum0 + lsum1 + lsum_early;
+        // Some row's tile sum above the limit or not finite, or a row without
+        // a shift yet: the exact path.
         float alpha = 1.f;
-        if constexpr (XS) {
-            if (__builtin_amdgcn_ballot_w64(wt.needs_exact_x(lsum)) != 0) alpha = wt.exact_shift_x(s_cur, pop, lsum);
-        } else {
-            if (__builtin_amdgcn_ballot_w64(!(lsum <= SHIFT_SUM_LIMIT)) != 0) alpha = wt.exact_shift(s_cur, pop, lsum);
-        }
+        if (__builtin_amdgcn_ballot_w64(wt.needs_exact_x(lsum)) != 0) alpha = wt.exact_shift_x(s_cur, pop, lsum);
         wt.l_run = alpha * wt.l_run + lsum;
         const float sh = wt.shift_base();  // for tile j+1's scores
 
         bf16x8 vop[3];
         vop[0] = wt.vread(vs_cur, 0);
         vop[1] = wt.vread(vs_cur, 1);
-        // XS: the next tile's scores are masked first (its early pairs are
-        // formed below); a masked -inf stays -inf when shifted.
-        if constexpr (XS && FULL) wt.mask(kb + (j + 1) * BC, ke, s_nxt);
+        // The next tile's scores are masked first (its early pairs are formed
+        // below); a masked -inf stays -inf when shifted.
+        if constexpr (FULL && !MASK_LATE) wt.mask(kb + (j + 1) * BC, ke, s_nxt);
         float le0 = 0.f, le1 = 0.f;
         fence();
 #pragma unroll
@@ -223,13 +213,13 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             const int t4 = slot / (D / 32), db = slot % (D / 32);
             wt.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[slot % 3], pop[t4], wt.oacc[db], 0, 0, 0);
             if (slot + 2 < PSLOTS) vop[(slot + 2) % 3] = wt.vread(vs_cur, slot + 2);
-            // The VALU is free here.  XS: tile j+1's scores are shifted,
-            // 32 / PSLOTS per slot.  With a bias: the bias of tile
+            // The VALU is free here.  Without a bias: tile j+1's scores are
+            // shifted, 32 / PSLOTS per slot.  With a bias: the bias of tile
             // j+1 (staged during the last iteration, landed with this
             // iteration's wait) goes into its scores, run by run; then tile
             // j+2's bias is fetched into the same region, once every read of
             // it has returned.
-            if constexpr (XS && FULL && !BIAS) {
+            if constexpr (FULL && !BIAS) {
 #pragma unroll
                 for (int u = 0; u < 32 / PSLOTS; u += 2) wt.shift_pair(s_nxt, slot * (32 / PSLOTS) + u, sh);
                 // early pair slot-1 (shifted in the previous slot)
@@ -239,7 +229,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
                 constexpr int PER = (8 + PSLOTS / 2 - 1) / (PSLOTS / 2);  // runs per slot over the first half
                 if (slot < PSLOTS / 2) {
 #pragma unroll
-                    for (int t = slot * PER; t < slot * PER + PER && t < 8; ++t) wt.bias_apply(bregion, t, lane, s_nxt, c, XS ? sh : 0.f);
+                    for (int t = slot * PER; t < slot * PER + PER && t < 8; ++t) wt.bias_apply(bregion, t, lane, s_nxt, c, sh);
                 }
                 if (slot == PSLOTS / 2 && bias_next) {
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -248,7 +238,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             }
             fence();
         }
-        if constexpr (XS && FULL) lsum_early = le0 + le1;
+        if constexpr (FULL) lsum_early = le0 + le1;
     };
     using Full = std::integral_constant<bool, true>;
     using Last = std::integral_constant<bool, false>;
@@ -295,11 +285,11 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         if (nw > 0) {
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) wt.score_step(lds_k0, kk, sa);
-            if constexpr (XS) {
+            {
                 // Tile 0 masked, shifted against base 0 (no shift yet) -- with
                 // a bias by adding it (landed with the prologue's wait) --,
                 // its early pairs formed.
-                wt.mask(kb, ke, sa);
+                if constexpr (!MASK_LATE) wt.mask(kb, ke, sa);
                 if constexpr (BIAS) {
 #pragma unroll
                     for (int t = 0; t < 8; ++t) wt.bias_apply(bregion, t, lane, sa, c, 0.f);
@@ -311,12 +301,6 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 #pragma unroll
                 for (int e = 0; e < 2 * EARLY; e += 2) wt.prob_pair_x(sa, e, popw, le);
                 lsum_early = le;
-            }
-            if constexpr (!XS && BIAS) {
-                // Tile 0's bias landed with the prologue's wait (the mask
-                // follows at the start of the first iteration).
-#pragma unroll
-                for (int t = 0; t < 8; ++t) wt.bias_apply(bregion, t, lane, sa, c, 0.f);
             }
             if constexpr (BIAS) {
                 // Tile 1's bias follows tile 0's.

@@ -26,14 +26,16 @@
 //
 // Lazy shift: the probabilities of a tile are first formed against the
 // current shift, with no row max.  Only when some row's tile sum exceeds 2^60
-// (or is not finite -- the first tile, where the shift is still -inf) does the
-// wave take the exact path: row max, new shift, rescale of l and o~, and the
-// probabilities again.  Any shift gives the same softmax as long as numerator
-// and denominator share it and nothing overflows.
+// or is not finite, or a row has no shift yet (its first tile with a visible
+// key), does the wave take the exact path: row max, new shift, rescale of l
+// and o~, and the probabilities again.  Any shift gives the same softmax as
+// long as numerator and denominator share it and nothing overflows.  A
+// tile's scores are brought to base-2 units against the shift (x = c*s - m)
+// before its softmax, while the previous tile's P.V MFMAs run.
 //
 // An additive score bias (an elementwise mask(), which eq. (8) leaves open)
-// is staged through LDS per wave and folded into the scores as
-// c * s + log2(e) * bias before the tile math, which then runs with c = 1.
+// is staged through LDS per wave and folded into the scores in the same FMA:
+// x = c * s + (log2(e) * bias - m).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -298,19 +300,6 @@ struct WaveTile {
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 
-    // Probabilities of scores e, e+1 (e even; register r of block cb is score
-    // 16*cb + r) against shift m, packed to bf16 into word e/2 of popw, their
-    // sum (of the rounded values) added to acc.
-    __device__ __forceinline__ void prob_pair(const f32x16 (&s)[2], int e, float m, uint32_t (&popw)[BC / 16][4],
-                                              float &acc) const {
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        const float p0 = exp2_fast(__builtin_fmaf(s[e >> 4][e & 15], c, -m));
-        const float p1 = exp2_fast(__builtin_fmaf(s[(e + 1) >> 4][(e + 1) & 15], c, -m));
-        const bf16x2 pp = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
-        popw[e >> 3][(e & 7) >> 1] = __builtin_bit_cast(uint32_t, pp);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
-    }
-
     // The shift a tile's scores are taken against before the tile is seen:
     // the running one, or 0 for a row that has no shift yet (no visible key
     // so far).
@@ -325,7 +314,9 @@ struct WaveTile {
         s[(e + 1) >> 4][(e + 1) & 15] = __builtin_fmaf(s[(e + 1) >> 4][(e + 1) & 15], c, -sh);
     }
 
-    // prob_pair for shifted scores x (shift_pair): P = 2^x.
+    // Probabilities of shifted scores e, e+1 (e even; register r of block cb
+    // is score 16*cb + r): P = 2^x, packed to bf16 into word e/2 of popw,
+    // their sum (of the rounded values) added to acc.
     __device__ __forceinline__ void prob_pair_x(const f32x16 (&x)[2], int e, uint32_t (&popw)[BC / 16][4],
                                                 float &acc) const {
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -361,26 +352,6 @@ struct WaveTile {
         const float alpha = m_new == NEG_INF ? 1.f : exp2_fast(m_run - m_new);  // 0 when m_run was -inf
         m_run = m_new;
         lsum = probs_scaled(x, 1.f, delta, pop);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        return alpha;
-    }
-
-    // Exact path of one tile: row max, new shift, rescale of o~ (l is rescaled
-    // by the caller with the returned factor) and the probabilities again.
-    // Returns the factor 2^(m_old - m_new); lsum receives the new tile sum.
-    __device__ __forceinline__ float exact_shift(const f32x16 (&s)[2], bf16x8 (&pop)[BC / 16], float &lsum) {
-        float mx = NEG_INF;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
-        mx = xhalf_max(mx);
-        const float m_new = fmaxf(m_run, mx * c);            // -inf stays -inf (c > 0)
-        const float m_use = m_new == NEG_INF ? 0.f : m_new;  // fully masked so far: p = 0
-        const float alpha = exp2_fast(m_run - m_use);         // 0 when m_run = -inf
-        m_run = m_new;
-        lsum = probs(s, m_use, pop);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
         return alpha;
