@@ -77,7 +77,8 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     constexpr bool MASK_LATE = BIAS && D == 128;
     // Probability pairs of the next tile formed during the P.V phase
     // (the rest in the score phase); their packed values and sum carry over.
-    // 4 of the 16 (paired A/B: c3 -1.4 %, c4 -0.3 %; 8 pairs gained nothing);
+    // 4 of the 16 (paired A/B: 2x16x4096^2 causal -1.4 %, 1x8x16384^2 causal
+    // -0.3 %; 2 or 6 pairs did worse, 8 gained nothing);
     // none with a bias, whose runs are added during the first half of the
     // P.V phase.
     constexpr int EARLY = BIAS ? 0 : 4;
@@ -112,10 +113,8 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     const u32x4 krs = make_rsrc(k + (size_t)bh * M * D, (uint32_t)M * T::RB);
     const u32x4 vrs = make_rsrc(v + (size_t)bh * M * D, (uint32_t)M * T::RB);
 
-    // With a bias the scores are brought to base-2 units (bias included)
-    // before the tile math, which then runs with c = 1.
     WaveTile<D, CAUSAL> wt;
-    wt.init(q + (size_t)bh * N * D, N, q0 + wave * 32, lane, BIAS ? 1.f : c, qsign, coff);
+    wt.init(q + (size_t)bh * N * D, N, q0 + wave * 32, lane, c, qsign, coff);
     // This lane's bias row as a byte offset into the bias buffer (rows past N
     // read row N - 1); the front end keeps the bias extent below 2^32 bytes.
     u32x4 brs{};
