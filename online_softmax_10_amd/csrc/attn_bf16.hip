@@ -296,6 +296,12 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
 #pragma unroll
                     for (int e = 0; e < 32; e += 2) wt.shift_pair(sa, e, 0.f);
                 }
+                // With tile 0 masked, its row max is the row's first shift, so
+                // the first iteration needs no exact path (a row with no
+                // visible key in tile 0 keeps none).  Unmasked (MASK_LATE), a
+                // masked key could set a shift under which the visible ones
+                // vanish: the exact path of the first iteration sets it then.
+                if constexpr (!MASK_LATE) wt.first_shift(sa);
                 float le = 0.f;
 #pragma unroll
                 for (int e = 0; e < 2 * EARLY; e += 2) wt.prob_pair_x(sa, e, popw, le);

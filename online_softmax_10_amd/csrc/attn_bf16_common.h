@@ -327,6 +327,25 @@ struct WaveTile {
         acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
     }
 
+    // A row's first shift from its first tile of shifted scores x = c*s
+    // (shift base 0, masked): m = max x, and x -= m in place.  A row with no
+    // visible key there keeps no shift.
+    __device__ __forceinline__ void first_shift(f32x16 (&x)[2]) {
+        float mx = NEG_INF;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[cb][r]);
+        mx = xhalf_max(mx);
+        if (mx != NEG_INF) {
+            m_run = mx;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[cb][r] -= mx;
+        }
+    }
+
     // Whether this lane's row needs the exact path for a tile of shifted
     // scores with probability sum lsum: the sum is above the limit or not
     // finite, or the row has no shift yet (its first tile: scores far below
