@@ -25,7 +25,7 @@
 // into one FMA before v_exp_f32; a negative scale flips q's sign bit on load.
 //
 // Lazy shift: the probabilities of a tile are first formed against the
-// current shift, with no row max.  Only when some row's tile sum exceeds 2^60
+// current shift, with no row max.  Only when some row's tile sum exceeds 2^40
 // or is not finite, or a row has no shift yet (its first tile with a visible
 // key), does the wave take the exact path: row max, new shift, rescale of l
 // and o~, and the probabilities again.  Any shift gives the same softmax as
@@ -62,14 +62,14 @@ constexpr int BC = kBf16KeyTile;  // keys per tile
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float LOG2E = 1.4426950408889634f;
-// Largest tile sum kept against a stale shift: 2^60.  Probabilities stay at
-// most 2^60 (bf16 keeps its 8-bit relative precision at any magnitude), and
-// the fp32 sums stay far below overflow (at most 2^60 per tile, 2^80 over a
-// million tiles; products with v stay below 2^128 for |v| < 2^68).  Against
-// a limit of 2^16 it spares exact paths on peaked softmaxes (1x8x16384^2
-// causal with logits up to +-54: -4.1 % per launch at 2^30, another -1 % at
-// 2^60; 2x16x4096^2 causal with N(0,1) inputs: unchanged).
-constexpr float SHIFT_SUM_LIMIT = 1152921504606846976.f;
+// Largest tile sum kept against a stale shift: 2^40.  Probabilities stay at
+// most 2^40 (bf16 keeps its 8-bit relative precision at any magnitude); the
+// fp32 sum and accumulator, at most 2^40 x |v| per tile, stay below overflow
+// for |v| < 2^68 over a million tiles.  Against a limit of 2^16 it spares
+// exact paths on peaked softmaxes (1x8x16384^2 causal with logits up to +-54:
+// -4.1 % per launch at 2^30, about -5 % at 2^40 and at 2^60; 2x16x4096^2
+// causal with N(0,1) inputs: unchanged).
+constexpr float SHIFT_SUM_LIMIT = 1099511627776.f;
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer descriptor, 32-bit data
 
 template <int D>
