@@ -156,6 +156,21 @@ def test_scores_far_below_zero(d, causal, splits):
     check_full(w, 11, splits=splits, qkv=tuple(si.f32_to_bf16_bits(x) for x in (q, k, v)))
 
 
+def test_peaked_softmax_large_values():
+    # Q, K with standard deviation 3 (peaked rows, the shift moves lazily, so
+    # probabilities up to the tile-sum limit) and V scaled by 2^50: products
+    # and sums stay finite, and O / 2^50 (an exact power-of-two scaling) meets
+    # the usual rule against the oracle on the unscaled V.
+    w = W["c4"].with_shape(H=2, N=1024, M=1024)
+    q, k, v = si.make_qkv(w, 5)
+    v_big = si.f32_to_bf16_bits(si.to_f64(v, "bf16").astype(np.float32) * np.float32(2.0 ** 50))
+    log("[gpu] peaked softmax, V scaled by 2^50")
+    o, lse = gpu_attention(q, k, v_big, "bf16", w.scale, True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    o_ref, lse_ref = oracle.attention(si.to_f64(q, "bf16"), si.to_f64(k, "bf16"), si.to_f64(v, "bf16"), w.scale, True)
+    compare(o / 2.0 ** 50, lse, o_ref, lse_ref, "bf16", "peaked, V x 2^50")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_query_uniform(dtype):
     w = si.Workload("zeroq", 1, 2, 160, 300, 64, dtype, True, "normal")
