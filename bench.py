@@ -80,7 +80,7 @@ COPY_MIB = 512  # size of the plain copy that calibrates the byte counters
 def counter_commands(wl: str, out_dir: str) -> list:
     """The four rocprofv3 counter runs (from the repository root, results
     under out_dir) that --traffic-from-counters reads back."""
-    run = f"python3 bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline"
+    run = f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --trials 0 --workload {wl}"
     cal = f"python3 bench.py --calibrate-copy {COPY_MIB} --steps 3"
     pmc = "timeout -s KILL 120 rocprofv3 --pmc"
     return [f"{pmc} FETCH_SIZE --output-format csv -d {out_dir}/pmc_fetch_{wl} -o run -- {run}",
@@ -144,8 +144,32 @@ def algorithmic_bytes(w: si.Workload) -> float:
     return w.B * w.H * ((w.N + 2 * w.M) * w.d * esz + w.N * w.d * esz + w.N * 4)
 
 
+def parity_rule(o, lse, o_ref, lse_ref, dtype: str) -> dict:
+    """The workloads' element-wise rule, applied to the GPU rows against the oracle's.
+
+    bf16: |o - o_ref| <= 1e-2 + half a bf16 ulp of o_ref (o is stored in bf16)
+    and |lse - lse_ref| <= 5e-3; fp32: 1e-5 on both."""
+    o = np.asarray(o, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    if dtype == "bf16":
+        a = np.abs(o_ref)
+        half_ulp = np.where(a > 0, np.exp2(np.floor(np.log2(np.where(a > 0, a, 1.0))) - 8.0), 0.0)
+        bound, lse_tol = 1e-2 + half_ulp, 5e-3
+        rule = "|do| <= 1e-2 + ulp_bf16(o_ref)/2, |dlse| <= 5e-3"
+    else:
+        bound, lse_tol = np.full_like(o_ref, 1e-5), 1e-5
+        rule = "|do| <= 1e-5, |dlse| <= 1e-5"
+    err_o = np.abs(o - o_ref)
+    err_l = np.abs(np.asarray(lse, dtype=np.float64) - np.asarray(lse_ref, dtype=np.float64))
+    ok = bool(np.all(np.isfinite(o)) and np.all(err_o <= bound) and np.all(err_l <= lse_tol))
+    return {"rule": rule, "pass": ok, "o_elements_over_bound": int(np.sum(~(err_o <= bound))),
+            "lse_over_bound": int(np.sum(~(err_l <= lse_tol))),
+            "max_abs_o": float(err_o.max(initial=0.0)), "max_abs_lse": float(err_l.max(initial=0.0))}
+
+
 def cpu_baseline(w: si.Workload, q, k, v, o_gpu, lse_gpu, target_s: float, bias=None):
-    """Time the oracle on an evenly spaced sample of query rows (~target_s seconds)."""
+    """Time the oracle on an evenly spaced sample of query rows (~target_s seconds)
+    and check the GPU's rows of that sample against it (the workloads' rule)."""
     import oracle
 
     err(f"[bench] cpu baseline: oracle on {oracle.num_threads()} threads")
@@ -179,8 +203,7 @@ def cpu_baseline(w: si.Workload, q, k, v, o_gpu, lse_gpu, target_s: float, bias=
         "sample": f"{count} of {total} query rows, evenly spaced over all heads and positions "
                   f"({flops / 1e9:.2f} GFLOP, {dt:.1f} s)",
         "seconds": dt,
-        "max_abs_err_vs_gpu": {"o": float(np.max(np.abs(o_s - o_ref))),
-                               "lse": float(np.max(np.abs(l_s - lse_ref)))},
+        "parity_vs_gpu": dict(parity_rule(o_s, l_s, o_ref, lse_ref, w.dtype), rows_checked=count),
     }
 
 
@@ -262,6 +285,33 @@ def bench_softmax(args, torch, osa) -> int:
         "max_abs_err_vs_oracle": err_max,
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_gemm(args, torch) -> int:
+    """torch.mm (hipBLASLt) on bf16 N x N matrices of N(0,1) values: the dense
+    matrix-core rate the chip sustains on random data, timed like attention."""
+    n = args.gemm_ceiling
+    g = torch.Generator(device="cuda").manual_seed(args.seed)
+    a = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    for _ in range(args.warmup):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        torch.mm(a, b, out=c)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"metric": "bf16 GEMM TFLOP/s (torch.mm, vendor library)", "value": round(tflops, 1),
+                      "unit": "TFLOP/s", "n": n, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(ms, 4), "pct_of_bf16_peak": round(100 * tflops / PEAKS_TFLOPS["bf16"], 2),
+                      "data": "N(0,1) bf16"}), flush=True)
     return 0
 
 
@@ -350,6 +400,11 @@ def main() -> int:
     ap.add_argument("--xent", default="", metavar="ROWSxN",
                     help="instead of attention, time softmax_xent (per-row cross-entropy + mean) on ROWS x N "
                          "float32 logits (e.g. 8192x32000)")
+    ap.add_argument("--trials", type=int, default=5,
+                    help="further timed regions of K steps each after the main one, reported as their median")
+    ap.add_argument("--gemm-ceiling", type=int, default=0, metavar="N",
+                    help="only time torch.mm on N x N bf16 matrices of N(0,1) values (the vendor GEMM): the "
+                         "matrix-core rate this chip sustains on random data, for comparison with attention")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--traffic-from-counters", default="", metavar="DIR",
@@ -386,6 +441,8 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": args.steps}), flush=True)
         return 0
+    if args.gemm_ceiling:
+        return bench_gemm(args, torch)
     if args.softmax:
         return bench_softmax(args, torch, osa)
     if args.xent:
@@ -452,6 +509,19 @@ def main() -> int:
 
     total_ms = t_begin.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    # Five further timed regions of K steps each: the spread between them
+    # (the clock falls under sustained matrix-core load) beside the main one.
+    trial_us = []
+    if args.trials > 0:
+        ta, tb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.trials):
+            torch.cuda.synchronize()
+            ta.record(stream)
+            for _ in range(args.steps):
+                step()
+            tb.record(stream)
+            torch.cuda.synchronize()
+            trial_us.append(ta.elapsed_time(tb) / args.steps * 1e3)
     if args.launch_events:
         launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
     else:
@@ -519,7 +589,16 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if trial_us:
+        line["trials"] = {"count": len(trial_us), "steps_each": args.steps,
+                          "us_per_step": [round(t, 2) for t in trial_us],
+                          "median_us_per_step": round(float(np.median(trial_us)), 2),
+                          "median_tflops": round(w.flops / (float(np.median(trial_us)) * 1e-6) / 1e12, 2),
+                          "note": "run after the main timed region, which alone gives value"}
     print(json.dumps(line), flush=True)
+    if cpu is not None and not cpu["parity_vs_gpu"]["pass"]:
+        err(f"[bench] the GPU output fails the parity rule against the oracle: {cpu['parity_vs_gpu']}")
+        return 1
     return 0
 
 

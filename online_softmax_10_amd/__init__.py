@@ -269,7 +269,7 @@ def plan(B, H, N, M, d, dtype="bf16", num_splits=0):
     Host-side query of the library's work decomposition; launches nothing.
     Raises ValueError for sizes the library rejects or with nothing to compute.
     """
-    code = {"bf16": ATTN_BF16, "f32": ATTN_F32}[dtype]
+    code = {"bf16": ATTN_BF16, "f32": ATTN_F32, "bf16_out_f32": ATTN_BF16_OUT_F32}[dtype]
     splits = ctypes.c_int(0)
     name = lib().attn_fwd_plan(B, H, N, M, d, code, num_splits, ctypes.byref(splits))
     if name is None:

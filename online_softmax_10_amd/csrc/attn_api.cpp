@@ -350,7 +350,7 @@ const char *attn_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int d, int
     const bool bf16 = dtype != ATTN_F32;
     const Plan plan = plan_for(B * H, N, M, d, bf16, num_splits);
     if (splits) *splits = plan.splits;
-    return main_kernel_name(main_kernel(plan, B * H, N, bf16));
+    return main_kernel_name(main_kernel(plan, B * H, N, bf16, false, dtype == ATTN_BF16_OUT_F32));
 }
 
 const char *attn_strerror(int code) {

@@ -121,10 +121,12 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
 // every outstanding load before each LDS read); completion is ordered
 // explicitly by wait_loads_and_barrier.  No memory clobber: the loads may be
 // scheduled among the LDS reads of other stages; they stay on their side of
-// the (volatile) barrier statements.  M0, the LDS base of the load, is a
-// register the compiler reserves and keeps no live value in here.
+// the (volatile) barrier statements.  M0 holds the LDS base of the load: the
+// "{m0}" operand makes the compiler set it (and know that it did).  A write
+// of M0 needs one wait state before an LDS-direct load reads it, and the
+// compiler's hazard check does not look inside the asm: hence the s_nop.
 __device__ __forceinline__ void lds_direct_load16(u32x4 rsrc, uint32_t lds_base, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(lds_base), "v"(voff), "s"(rsrc));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_base));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

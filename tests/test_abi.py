@@ -148,6 +148,8 @@ def test_plan_kernel_choice():
     # regimes between them.
     assert osa.plan(2, 16, 4096, 4096, 128) == ("attn_fwd_bf16_w8_kernel", 1)
     assert osa.plan(1, 8, 16384, 16384, 128) == ("attn_fwd_bf16_w8_kernel", 1)
+    assert osa.plan(2, 16, 4096, 4096, 64) == ("attn_fwd_bf16_w8_kernel", 1)
+    assert osa.plan(2, 16, 4096, 4096, 128, dtype="bf16_out_f32") == ("attn_fwd_bf16_w8_kernel", 1)
     assert osa.plan(4, 8, 1024, 1024, 64) == ("attn_fwd_bf16_kernel", 1)
     name, s = osa.plan(32, 32, 1, 8192, 128)
     assert name == "attn_decode_kernel" and 1 <= s <= osa.ATTN_MAX_SPLITS

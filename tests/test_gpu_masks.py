@@ -54,9 +54,13 @@ CASES = [
     (W("m", 4, 4, 1, 5000, 128, "bf16", True, "normal"), "bottom_right", [4000, 123, 5000, 0], 0),
     (W("m", 2, 4, 4, 3000, 64, "bf16", True, "normal"), "bottom_right", [3000, 1], 0),
     (W("m", 2, 2, 3, 900, 128, "f32", False, "normal"), False, [899, 2], 0),
-    # eight-wave width (>= 256 workgroups of 256 rows)
+    # 256-row widths (>= 256 workgroups of 256 rows): eight waves at d = 64,
+    # 64 rows per wave at d = 128
     (W("m", 2, 128, 512, 700, 64, "bf16", True, "normal"), "bottom_right", [700, 301], 0),
     (W("m", 2, 128, 300, 260, 128, "bf16", True, "normal"), "top_left", [260, 1], 0),
+    (W("m", 2, 128, 300, 700, 128, "bf16", True, "normal"), "bottom_right", [700, 333], 0),
+    (W("m", 2, 128, 520, 300, 128, "bf16", True, "normal"), "bottom_right", [300, 0], 0),
+    (W("m", 2, 128, 257, 1000, 128, "bf16", False, "normal"), False, [31, 1000], 0),
 ]
 
 

@@ -31,7 +31,7 @@ def _run(w, seed, out_dtype=None, splits=0, **kw):
     return (q, k, v), o, lse
 
 
-@pytest.mark.parametrize("wl,count", [("c4", 192), ("c3", 256), ("c2", 0)])
+@pytest.mark.parametrize("wl,count", [("c4", 0), ("c3", 0), ("c2", 0)])
 def test_literal_bf16_bound_with_f32_output(wl, count):
     import torch
 
