@@ -40,8 +40,9 @@ import seeded_inputs as si  # noqa: E402
 
 PEAKS_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16_common.h", "attn_f32.hip", "attn_decode.hip",
-                  "attn_api.cpp", "kernels.h"]
+# Device code of the attention kernels: the stamp of the committed traffic
+# figures (host-side planning is covered by the kernel name they record).
+KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16_common.h", "attn_f32.hip", "attn_decode.hip"]
 
 
 def err(msg: str) -> None:

@@ -5,45 +5,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_plan.h"
+
 namespace osa {
 
-// One attention problem, already validated by the front end.
-struct AttnProblem {
-    const void *q, *k, *v;  // [BH,N,d] / [BH,M,d] / [BH,M,d], dtype elements
-    void *o;                 // [BH,N,d] dtype (unused when writing partials)
-    float *lse;              // [BH,N]          (unused when writing partials)
-    int BH, N, M, d;
-    int H;                   // heads per batch (batch of head bh = bh / H)
-    const int32_t *kv_len;   // [B] valid keys per batch (device; clamped to [0, M]), or nullptr
-    // Additive score bias, fp32, or nullptr: element (b, h, i, j) at
-    // bias[b*bias_sb + h*bias_sh + i*bias_sn + j]; 16-byte aligned rows.
-    const float *bias;
-    uint32_t bias_bytes;     // bytes from bias to the end of its last element (< 2^32)
-    int64_t bias_sb, bias_sh, bias_sn;
-    int causal_off;          // causal: key j visible for query i iff j <= i + causal_off
-    float c;                 // |scale| * log2(e): scores are kept in base-2 units
-    bool negate_q;           // scale < 0: q's sign is flipped on load so c >= 0
-    bool causal;
-    bool out_f32;            // bf16 inputs, float32 o: single pass uses the partial-store path on o
-    // Split over keys: split s covers tiles [s*tiles_per_split, (s+1)*tiles_per_split)
-    // of the kernel's key tile size.  splits == 1 writes o and lse directly.
-    int splits;
-    int tiles_per_split;
-    float *part_o;           // [splits,BH,N,d] fp32, normalised partial outputs
-    float *part_lse;         // [splits,BH,N]   fp32, natural-log partial LSE (-inf if empty)
-};
-
-// Key tile sizes (the unit of a split range) of each kernel family.
-constexpr int kBf16KeyTile = 64;
-constexpr int kF32KeyTile = 32;
-constexpr int kDecodeKeyTile = 64;
-constexpr int kDecodeMaxQueries = 4;
+// Launches a call planned by plan_attn; a split plan's partials go to
+// `workspace` (at least plan.workspace_bytes of device memory, stream-ordered
+// on `stream`).  Returns ATTN_OK or ATTN_ERR_HIP (detail recorded).
+int launch_planned(const PlannedCall &plan, void *workspace, hipStream_t stream);
+// Records the detail string that attn_last_error_detail returns.
+void set_hip_detail(const char *what, hipError_t e);
 
 // Four-wave bf16 kernel: 128 query rows per workgroup (any size; split partials).
 hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream);
 // Eight-wave bf16 kernel: 256 query rows per workgroup, single pass only.
 hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream);
-constexpr int kBf16WideRows = 256;
 hipError_t launch_attn_f32(const AttnProblem &p, hipStream_t stream);
 // Few queries per head (N <= kDecodeMaxQueries), bf16 or fp32 inputs, always
 // writes partials (p.splits >= 1).
