@@ -42,7 +42,8 @@ enum {
     ATTN_ERR_HIP = -7,       /* a HIP launch or allocation failed (see attn_last_error_detail) */
     ATTN_ERR_SCALE = -8,     /* scale is NaN or infinite */
     ATTN_ERR_SPLITS = -9,    /* num_splits outside [0, ATTN_MAX_SPLITS] */
-    ATTN_ERR_MASK = -10      /* attn_mask.causal is not one of attn_causal */
+    ATTN_ERR_MASK = -10,     /* attn_mask.causal is not one of attn_causal */
+    ATTN_ERR_WORKSPACE = -11 /* attn_fwd_masked_noalloc: the split workspace exceeds its static scratch */
 };
 
 /* Largest split count attn_fwd_splits accepts. */
@@ -162,6 +163,29 @@ typedef struct attn_mask {
 int attn_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse,
                     int64_t B, int64_t H, int64_t N, int64_t M, int d,
                     float scale, const attn_mask *mask, int dtype, int num_splits, void *stream);
+
+/*
+ * attn_fwd_masked_noalloc -- attn_fwd_masked for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments, plan, kernels and results as attn_fwd_masked (bit for
+ * bit), but a split plan's partials (num_splits * B*H*N * (d + 1) * 4 bytes)
+ * go to a static device array of ATTN_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on until the process ends; nothing is
+ * allocated or freed.  The array of the current device is used (the stream
+ * must belong to it).  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other host threads) race, so the
+ * caller orders them.  Nothing in the array needs clearing between calls.
+ *
+ * Errors as attn_fwd_masked, plus ATTN_ERR_WORKSPACE, before any HIP call,
+ * when the split workspace would exceed ATTN_NOALLOC_SCRATCH_BYTES (choose
+ * fewer splits, or num_splits = 1 for the single pass, which needs none).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES 33554432
+int attn_fwd_masked_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int64_t B, int64_t H, int64_t N, int64_t M, int d,
+                            float scale, const attn_mask *mask, int dtype, int num_splits, void *stream);
 
 /*
  * attn_fwd_kv_outer -- the same attention as attn_fwd, computed in the

@@ -16,7 +16,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "fwd_splits", "fwd_kv_outer", "online_softmax", "logsumexp", "softmax_xent", "plan", "lib", "AttnMask", "CAUSAL_MODES", "LIB_PATH", "AttnError",
+__all__ = ["fwd", "fwd_splits", "fwd_noalloc", "fwd_kv_outer", "NOALLOC_SCRATCH_BYTES", "online_softmax", "logsumexp", "softmax_xent", "plan", "lib", "AttnMask", "CAUSAL_MODES", "LIB_PATH", "AttnError",
            "ATTN_F32", "ATTN_BF16", "ATTN_BF16_OUT_F32", "ATTN_MAX_SPLITS", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -25,10 +25,12 @@ ATTN_F32 = 0
 ATTN_BF16 = 1
 ATTN_BF16_OUT_F32 = 2
 ATTN_MAX_SPLITS = 256
+NOALLOC_SCRATCH_BYTES = 33554432  # ATTN_NOALLOC_SCRATCH_BYTES
 ERROR_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEADDIM",
                -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_OVERFLOW", -7: "ATTN_ERR_HIP",
-               -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_SPLITS", -10: "ATTN_ERR_MASK"}
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "attn_fwd_masked", "attn_fwd_kv_outer", "online_softmax",
+               -8: "ATTN_ERR_SCALE", -9: "ATTN_ERR_SPLITS", -10: "ATTN_ERR_MASK", -11: "ATTN_ERR_WORKSPACE"}
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_splits", "attn_fwd_masked", "attn_fwd_masked_noalloc", "attn_fwd_kv_outer",
+                    "online_softmax",
                     "online_softmax_lse", "softmax_xent", "attn_fwd_plan", "attn_strerror", "attn_last_error_detail")
 
 # attn_causal of include/attn.h, by the names fwd() accepts.
@@ -72,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                       ctypes.POINTER(AttnMask), ctypes.c_int, ctypes.c_int, vp]
         L.attn_fwd_masked.restype = ctypes.c_int
+        L.attn_fwd_masked_noalloc.argtypes = L.attn_fwd_masked.argtypes
+        L.attn_fwd_masked_noalloc.restype = ctypes.c_int
         L.attn_fwd_kv_outer.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                         ctypes.c_int, ctypes.c_int, vp]
         L.attn_fwd_kv_outer.restype = ctypes.c_int
@@ -146,8 +150,18 @@ def _bias_operand(bias, B, H, N, M, device):
     return view, st[:3]
 
 
+def fwd_noalloc(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None, kv_len=None, bias=None,
+                out_dtype=None):
+    """fwd_splits through attn_fwd_masked_noalloc: the split workspace is the
+    library's static device scratch (NOALLOC_SCRATCH_BYTES per GPU) instead of
+    a stream-ordered allocation.  Pass out and lse to allocate nothing at all.
+    Calls that overlap on one GPU race on the scratch."""
+    return fwd_splits(q, k, v, scale=scale, causal=causal, num_splits=num_splits, out=out, lse=lse, kv_len=kv_len,
+                      bias=bias, out_dtype=out_dtype, _noalloc=True)
+
+
 def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=None, kv_len=None, bias=None,
-               out_dtype=None):
+               out_dtype=None, _noalloc=False):
     """Attention forward with an explicit split count (0 = library's choice).
 
     q [B,H,N,d], k and v [B,H,M,d]: contiguous CUDA/HIP tensors of one dtype
@@ -195,7 +209,7 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
     if causal not in CAUSAL_MODES:
         raise ValueError(f"causal must be one of {sorted(map(str, CAUSAL_MODES))}, got {causal!r}")
     mode = CAUSAL_MODES[causal]
-    if kv_len is None and mode != 2 and bias is None:
+    if kv_len is None and mode != 2 and bias is None and not _noalloc:
         rc = lib().attn_fwd_splits(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                    B, H, N, M, d, float(scale), mode, code, int(num_splits),
                                    _stream_handle(q.device))
@@ -210,11 +224,11 @@ def fwd_splits(q, k, v, scale=None, causal=False, num_splits=0, out=None, lse=No
     if bias is not None:
         bias, (sb, sh, sn) = _bias_operand(bias, B, H, N, M, q.device)
         mask.bias, mask.bias_stride_b, mask.bias_stride_h, mask.bias_stride_n = bias.data_ptr(), sb, sh, sn
-    rc = lib().attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                               B, H, N, M, d, float(scale), ctypes.byref(mask), code, int(num_splits),
-                               _stream_handle(q.device))
+    entry = lib().attn_fwd_masked_noalloc if _noalloc else lib().attn_fwd_masked
+    rc = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+               B, H, N, M, d, float(scale), ctypes.byref(mask), code, int(num_splits), _stream_handle(q.device))
     if rc != 0:
-        raise AttnError(rc, "attn_fwd_masked")
+        raise AttnError(rc, "attn_fwd_masked_noalloc" if _noalloc else "attn_fwd_masked")
     return out, lse
 
 

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["attn_api.cpp", "attn_plan.cpp", "attn_bf16.hip", "attn_f32.hip", "attn_decode.hip",
+SOURCES = ["attn_api.cpp", "attn_plan.cpp", "attn_bf16.hip", "attn_noalloc.hip", "attn_f32.hip", "attn_decode.hip",
            "online_softmax.hip", "softmax_xent.hip", "attn_kv_outer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

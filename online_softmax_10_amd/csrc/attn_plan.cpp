@@ -236,6 +236,7 @@ const char *attn_strerror(int code) {
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_SPLITS: return "num_splits outside [0, ATTN_MAX_SPLITS]";
     case ATTN_ERR_MASK: return "unknown causal mode in attn_mask";
+    case ATTN_ERR_WORKSPACE: return "the split workspace exceeds the static scratch (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown error code";
     }
 }

@@ -217,6 +217,23 @@ def test_bias_validation(L, buf):
     assert f(*big(2**30)) == OVERFLOW
 
 
+def test_noalloc_validation(L, buf):
+    # attn_fwd_masked_noalloc validates like attn_fwd_masked and rejects a split
+    # workspace beyond its static scratch, all before any HIP call.
+    f = L.attn_fwd_masked_noalloc
+    args = lambda mask, **kw: (buf, buf, buf, buf, buf, kw.get("B", 1), kw.get("H", 1), kw.get("N", 4),
+                               kw.get("M", 4), kw.get("d", 64), 0.125, mask, 1, kw.get("splits", 0), None)
+    assert f(*args(ctypes.byref(osa.AttnMask(3, None)))) == -10
+    assert f(*args(None, B=0)) == OK
+    assert f(*args(None, splits=-1)) == SPLITS
+    assert f(*args(None, d=96)) == HEADDIM
+    # 256 splits x 300 rows x (128 + 1) floats = 39.6 MB > 32 MiB
+    assert f(*args(None, N=300, M=300000, d=128, splits=256)) == -11  # ATTN_ERR_WORKSPACE
+    assert 256 * 300 * 129 * 4 > osa.NOALLOC_SCRATCH_BYTES
+    with open(HEADER, encoding="utf-8") as h:
+        assert int(re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES (\d+)", h.read()).group(1)) == osa.NOALLOC_SCRATCH_BYTES
+
+
 def test_masked_validation(L, buf):
     f = L.attn_fwd_masked
     m = osa.AttnMask(3, None)
