@@ -103,9 +103,11 @@ void oracle_xent_f64(const double *x, const int64_t *labels, double *loss, doubl
 }
 
 /*
- * The one-pass normaliser recurrence, element by element:
- *   m_i = max(m_{i-1}, x_i),   s_i = s_{i-1} * e^{m_{i-1} - m_i} + e^{x_i - m_i},
- * started from m_1 = x_1, s_1 = 1.
+ * The one-pass normaliser: the pair (m, s) of a prefix of the row -- its
+ * maximum and the sum of e^{x - m} over it -- extended by one element at a
+ * time, m' = max(m, x_i) and s' = s e^{m - m'} + e^{x_i - m'}.  The empty
+ * prefix is (m, s) = (-inf, 0) and contributes nothing when it is carried to
+ * the first finite maximum; leading -inf elements leave it empty.
  * Source: "Online Softmax and Flash Attention" page, section "Online softmax",
  * eq. (3)-(5); "Softmax与Flash-Attention" page, "online-softmax 推导".
  * Writes the final m_N and s_N of each row.  Kept only to check that s_N equals
@@ -118,12 +120,15 @@ void oracle_online_normalizer_f64(const double *x, double *m_out, double *s_out,
 #pragma omp parallel for schedule(static)
     for (r = 0; r < rows; ++r) {
         const double *xr = x + r * n;
-        double m = xr[0];
-        double s = 1.0;
-        for (int64_t i = 1; i < n; ++i) {
-            double m_new = xr[i] > m ? xr[i] : m;
-            s = s * exp(m - m_new) + exp(xr[i] - m_new);
-            m = m_new;
+        double m = -INFINITY; /* the empty prefix */
+        double s = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            const double m_next = xr[i] > m ? xr[i] : m;
+            if (m_next == -INFINITY)
+                continue;
+            const double carried = m == -INFINITY ? 0.0 : s * exp(m - m_next);
+            s = carried + exp(xr[i] - m_next);
+            m = m_next;
         }
         m_out[r] = m;
         s_out[r] = s;

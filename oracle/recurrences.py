@@ -26,20 +26,23 @@ def _exp(t: float) -> float:
 def two_loop_row(x, V):
     """Attention for one query row from its scores x[0..M-1] and V [M, d].
 
-    Loop 1 (online normaliser over the scores): g_m = max(g_{m-1}, x_m),
-    s_m = s_{m-1} e^{g_{m-1}-g_m} + e^{x_m-g_m}.  Loop 2: y_m = e^{x_m-g_M}/s_M
-    and A_m = A_{m-1} + y_m V[m,:].
+    Loop 1 carries the normaliser (g, s) of the scores seen so far -- their
+    maximum and their sum of e^{x - g} -- from the empty prefix (-inf, 0),
+    one score at a time: g' = max(g, x_m), s' = s e^{g - g'} + e^{x_m - g'}.
+    Loop 2 sums the normalised weights e^{x_m - g_M} / s_M times V[m,:].
     Source: "Online Softmax and Flash Attention" page, eq. (10)-(13) (loop 1)
     and eq. (14)-(15) (loop 2).
     Returns (A_M, g_M, s_M).
     """
     x = [float(t) for t in x]
     V = np.asarray(V, dtype=np.float64)
-    g, s = x[0], 1.0
-    for m in range(1, len(x)):
-        g_new = max(g, x[m])
-        s = s * _exp(g - g_new) + _exp(x[m] - g_new)
-        g = g_new
+    g, s = NEG_INF, 0.0
+    for xm in x:
+        g_next = max(g, xm)
+        if g_next == NEG_INF:
+            continue  # only -inf so far: the prefix stays empty
+        s = s * _exp(g - g_next) + _exp(xm - g_next)
+        g = g_next
     A = np.zeros(V.shape[1])
     for m in range(len(x)):
         A = A + (_exp(x[m] - g) / s) * V[m]
@@ -49,21 +52,25 @@ def two_loop_row(x, V):
 def stepwise_normalised_row(x, V):
     """The single fused loop with a normalised accumulator A'.
 
-    A'_1 = e^{x_1-g_1}/s_1 V_1 and
-    A'_m = A'_{m-1} s_{m-1} e^{g_{m-1}-g_m} / s_m + e^{x_m-g_m}/s_m V_m,
-    so that A'_M equals the attention row.
+    The state (g, s, A') of the scores seen so far -- maximum, sum of
+    e^{x - g}, and the attention row over just those keys -- starts empty
+    ((-inf, 0, 0)) and takes one key at a time: with g' = max(g, x_m) and
+    s' = s e^{g - g'} + e^{x_m - g'}, the old row keeps the weight
+    s e^{g - g'} / s' and V[m] gets e^{x_m - g'} / s'.  A'_M is the row.
     Source: "Online Softmax and Flash Attention" page, eq. (20)-(22) and (26).
     Returns (A'_M, g_M, s_M).
     """
     x = [float(t) for t in x]
     V = np.asarray(V, dtype=np.float64)
-    g, s = x[0], 1.0
-    A = (_exp(x[0] - g) / s) * V[0]
-    for m in range(1, len(x)):
-        g_new = max(g, x[m])
-        s_new = s * _exp(g - g_new) + _exp(x[m] - g_new)
-        A = A * (s * _exp(g - g_new) / s_new) + (_exp(x[m] - g_new) / s_new) * V[m]
-        g, s = g_new, s_new
+    g, s = NEG_INF, 0.0
+    A = np.zeros(V.shape[1])
+    for xm, vm in zip(x, V):
+        g_next = max(g, xm)
+        if g_next == NEG_INF:
+            continue  # only -inf so far: the state stays empty
+        s_next = s * _exp(g - g_next) + _exp(xm - g_next)
+        A = A * (s * _exp(g - g_next) / s_next) + (_exp(xm - g_next) / s_next) * vm
+        g, s = g_next, s_next
     return A, g, s
 
 

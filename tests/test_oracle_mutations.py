@@ -42,10 +42,12 @@ MUTATIONS = [
      "        for (int64_t j = 1; j < n; ++j)\n            if (xr[j] > m) m = xr[j];",
      "double *yr = y + r * n;\n        /* pass 1: the maximum */\n        double m = xr[0];\n"
      "        for (int64_t j = 1; j < n; ++j)\n            if (xr[j] < m) m = xr[j];"),
-    ("normaliser without the rescale", "s = s * exp(m - m_new) + exp(xr[i] - m_new);", "s = s + exp(xr[i] - m_new);"),
-    ("normaliser rescale inverted", "s = s * exp(m - m_new) + exp(xr[i] - m_new);",
-     "s = s * exp(m_new - m) + exp(xr[i] - m_new);"),
-    ("normaliser starts at 0", "double s = 1.0;", "double s = 0.0;"),
+    ("normaliser without the rescale", "const double carried = m == -INFINITY ? 0.0 : s * exp(m - m_next);",
+     "const double carried = m == -INFINITY ? 0.0 : s;"),
+    ("normaliser rescale inverted", "const double carried = m == -INFINITY ? 0.0 : s * exp(m - m_next);",
+     "const double carried = m == -INFINITY ? 0.0 : s * exp(m_next - m);"),
+    ("normaliser's empty prefix with maximum 0", "double m = -INFINITY; /* the empty prefix */",
+     "double m = 0.0; /* the empty prefix */"),
     ("LSE of softmax rows without the max", "lse[r] = m + log(s);", "lse[r] = log(s);"),
     ("query row ignores the head", "const double *qi = q + r * d;", "const double *qi = q + i * d;"),
     ("every head uses head 0's keys", "const double *kh = k + bh * M * d;", "const double *kh = k;"),
