@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from parity import compare, log, to_device
+from parity import compare, f32_bounds, log, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,12 @@ def run_bias(w, causal, bshape, kind="normal", kv_len=None, splits=0, neg_inf_fr
     log(f"  rows with no finite score: {int((~vis).sum())}")
     assert np.all(o[~vis] == 0.0), "rows with no finite score must give o = 0"
     assert np.all(np.isneginf(lse[~vis])), "rows with no finite score must give lse = -inf"
-    compare(o[vis], lse[vis], o_ref[vis], lse_ref[vis], w.dtype, f"bias {bshape} {causal}")
+    bounds = None
+    if w.dtype == "f32":
+        bo, bl = f32_bounds(si.to_f64(q, w.dtype), si.to_f64(k, w.dtype), si.to_f64(v, w.dtype), w.scale, causal,
+                            kv_len=kv_len, bias=bias.astype(np.float64))
+        bounds = (bo[vis], bl[vis])
+    compare(o[vis], lse[vis], o_ref[vis], lse_ref[vis], w.dtype, f"bias {bshape} {causal}", bounds)
     return int((~vis).sum())
 
 

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from parity import compare, log, to_device
+from parity import compare, f32_bounds, log, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -60,12 +60,12 @@ def test_random_problem(case):
     vis = np.isfinite(lse_ref)
     assert np.all(o[~vis] == 0.0) and np.all(np.isneginf(lse[~vis])), "rows with no finite score"
     if vis.any():
-        # fp32 bound scaled by the largest scaled logit (bias included), as for the other fp32 stress cases
-        s = np.einsum("bhnd,bhmd->bhnm", si.to_f64(q, w.dtype), si.to_f64(k, w.dtype)) * w.scale
-        if bias is not None:
-            s = s + np.broadcast_to(bias.astype(np.float64), s.shape)
-        logit_max = float(np.max(np.abs(s[np.isfinite(s)]))) if np.isfinite(s).any() else 8.0
-        compare(o[vis], lse[vis], o_ref[vis], lse_ref[vis], w.dtype, f"fuzz {case}", logit_max=max(8.0, logit_max))
+        bounds = None
+        if w.dtype == "f32":
+            bo, bl = f32_bounds(si.to_f64(q, w.dtype), si.to_f64(k, w.dtype), si.to_f64(v, w.dtype), w.scale, causal,
+                                kv_len=kv_len, bias=None if bias is None else bias.astype(np.float64))
+            bounds = (bo[vis], bl[vis])
+        compare(o[vis], lse[vis], o_ref[vis], lse_ref[vis], w.dtype, f"fuzz {case}", bounds)
 
 
 @pytest.mark.parametrize("N,M,causal,dtype", [(1, 300001, False, "bf16"), (5, 262147, "bottom_right", "bf16"),
@@ -83,5 +83,8 @@ def test_long_key_range(N, M, causal, dtype):
     o, lse = osa.fwd(qd, kd, vd, scale=w.scale, causal=causal)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention(si.to_f64(q, dtype), si.to_f64(k, dtype), si.to_f64(v, dtype), w.scale, causal)
+    bounds = None
+    if dtype == "f32":
+        bounds = f32_bounds(si.to_f64(q, dtype), si.to_f64(k, dtype), si.to_f64(v, dtype), w.scale, causal)
     compare(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, dtype,
-            f"long keys M={M}")
+            f"long keys M={M}", bounds)
