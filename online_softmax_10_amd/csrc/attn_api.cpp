@@ -35,9 +35,10 @@ int osa::launch_planned(const osa::PlannedCall &plan, void *workspace, hipStream
     osa::AttnProblem p = plan.p;
     if (!plan.split) {
         const bool w8 = plan.kernel == osa::MainKernel::BF16_8W || plan.kernel == osa::MainKernel::BF16_8W_BIAS;
-        const hipError_t e = plan.kernel == osa::MainKernel::F32 ? osa::launch_attn_f32(p, stream)
-                             : w8                            ? osa::launch_attn_bf16_w8(p, stream)
-                                                             : osa::launch_attn_bf16(p, stream);
+        const hipError_t e = plan.kernel == osa::MainKernel::F32         ? osa::launch_attn_f32(p, stream)
+                             : plan.kernel == osa::MainKernel::F32_SMALL ? osa::launch_attn_f32_small(p, stream)
+                             : w8                                        ? osa::launch_attn_bf16_w8(p, stream)
+                                                                         : osa::launch_attn_bf16(p, stream);
         if (e != hipSuccess) {
             set_detail("attention kernel launch", e);
             return ATTN_ERR_HIP;

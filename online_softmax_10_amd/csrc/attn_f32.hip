@@ -32,6 +32,7 @@ constexpr int BC = kF32KeyTile;  // 32 keys per tile
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994531f;
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor, 32-bit data
 
 template <int D>
 struct Layout {
@@ -48,6 +49,24 @@ __device__ __forceinline__ float xhalf_max(float x) {
 __device__ __forceinline__ float xhalf_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Q^T operand: lane (query row, half hh) holds q[row][2*kk + hh], kk < D/2,
+// times qsign (0 for a row past N).  Whole 16-byte chunks of a row that
+// exists (rows past N read row N - 1), all issued before any is used.
+template <int D>
+__device__ __forceinline__ void load_q_operand(const float *qh, int N, int row, int hh, float qsign,
+                                               float (&qop)[D / 2]) {
+    const float *qr = qh + (size_t)min(row, N - 1) * D;
+    const float f = row < N ? qsign : 0.f;
+    f32x4 x[D / 4];
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) x[i] = *reinterpret_cast<const f32x4 *>(qr + 4 * i);
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+        qop[2 * i] = (hh ? x[i][1] : x[i][0]) * f;
+        qop[2 * i + 1] = (hh ? x[i][3] : x[i][2]) * f;
+    }
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
@@ -97,8 +116,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
 
     // Q^T operand: lane (query l32, half hh) holds q[qrow][2*kk + hh].
     float qop[D / 2];
-#pragma unroll
-    for (int kk = 0; kk < D / 2; ++kk) qop[kk] = qrow < N ? qh[(size_t)qrow * D + 2 * kk + hh] * qsign : 0.f;
+    load_q_operand<D>(qh, N, qrow, hh, qsign, qop);
 
     f32x4 kreg[Lay::LOADS], vreg[Lay::LOADS];
     auto fetch = [&](int kv0) {
@@ -234,6 +252,215 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
         }
 }
 
+// Small problems: one workgroup per 32-row query block, its KW waves each
+// taking every KW-th key tile (a split over keys inside the workgroup; tiles
+// interleaved so causal ranges share out evenly), with K and V staged in each
+// wave's own LDS region.  Each wave keeps the running max, sum and
+// unnormalised accumulator of its tiles; at the end the waves' states are
+// merged in LDS with the same rule as any two blocks of the recurrence
+// (L = sum_w l_w 2^{m_w - M}, O = sum_w o~_w 2^{m_w - M} / L, M the largest
+// m_w): "从原始Softmax到在线Softmax" page, the merge of two (m, l, o~)
+// states.  One launch, no workspace.  No bias (the four-wave kernel above
+// takes those).
+template <int D>
+struct Small {
+    static constexpr int KW = D == 64 ? kF32SmallWaves64 : kF32SmallWaves128;  // waves per workgroup
+    static constexpr int KS = D + 2, VS = D + 8;         // LDS row strides (floats), as above
+    static constexpr int REGION = BC * (KS + VS);        // floats per wave: a K tile and a V tile
+    static constexpr int LOADS = BC * D / 4 / 64;        // float4 chunks per lane per tile (K and V each)
+    static constexpr int OS = D + 4;                     // row stride (floats) of a wave's scaled o~ in the merge
+    static_assert(REGION >= 32 * OS + 64, "the merge state fits a wave's region");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * Small<D>::KW, 1) void attn_fwd_f32_small_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v, float *__restrict__ o,
+    float *__restrict__ lse, int BH, int N, int M, float c, float qsign, int nrb, const int32_t *__restrict__ kv_len,
+    int H, int coff) {
+    using S = Small<D>;
+    __shared__ __attribute__((aligned(16))) float smem[S::KW * S::REGION];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    float *Ks = smem + wave * S::REGION;
+    float *Vs = Ks + BC * S::KS;
+
+    // Workgroup -> (head, 32-row block); the longest causal blocks first.
+    const int bh = blockIdx.x % BH;
+    const int rb = nrb - 1 - blockIdx.x / BH;
+    const int r0 = rb * 32;
+    const int qrow = r0 + l32;
+    int ke = M;
+    if (kv_len != nullptr) ke = min(ke, max(kv_len[bh / H], 0));
+    if (CAUSAL) ke = min(ke, r0 + 32 + coff);
+    const int ntiles = ke > 0 ? (ke + BC - 1) / BC : 0;
+
+    const float *qh = q + (size_t)bh * N * D;
+    const float *kh = k + (size_t)bh * M * D;
+    const float *vh = v + (size_t)bh * M * D;
+    // This wave's next tile in registers, read through buffer descriptors
+    // that end at key ke, so keys at or past ke (and whole tiles past the
+    // last) read as 0 without a branch; they are masked.  The first tile is
+    // requested before Q so that the two arrive in one round trip; each later
+    // tile is requested while the tile before it is in the matrix cores.
+    const int kv_bytes = max(ke, 0) * D * 4;  // ke <= M <= 1024 here
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(kh), 0, kv_bytes,
+                                                                         kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(vh), 0, kv_bytes,
+                                                                         kBufferWord3);
+    f32x4 kr[S::LOADS], vr[S::LOADS];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < S::LOADS; ++i) {
+            const int id = lane + 64 * i;
+            const int off = ((t * BC + id / (D / 4)) * D + 4 * (id % (D / 4))) * 4;
+            kr[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+            vr[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+        }
+    };
+    load_tile(wave);
+    float qop[D / 2];
+    load_q_operand<D>(qh, N, qrow, hh, qsign, qop);
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+    float m_run = NEG_INF;
+    float l_run = 0.f;
+
+    for (int t = wave; t < ntiles; t += S::KW) {
+        const int kv0 = t * BC;
+        __builtin_amdgcn_wave_barrier();  // the wave is done reading the previous tile
+#pragma unroll
+        for (int i = 0; i < S::LOADS; ++i) {
+            const int id = lane + 64 * i;
+            const int row = id / (D / 4), c4 = id % (D / 4);
+            float *kd = &Ks[row * S::KS + 4 * c4];
+            kd[0] = kr[i][0];
+            kd[1] = kr[i][1];
+            kd[2] = kr[i][2];
+            kd[3] = kr[i][3];
+            *reinterpret_cast<f32x4 *>(&Vs[row * S::VS + 4 * c4]) = vr[i];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        load_tile(t + S::KW);  // zeros once past the last tile
+        f32x16 s = f32x16{};
+        const float *krow = &Ks[l32 * S::KS + hh];
+#pragma unroll
+        for (int kk = 0; kk < D / 2; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * kk], qop[kk], s, 0, 0, 0);
+        // The next tile's loads go out one per two products of this tile.
+#pragma unroll
+        for (int i = 0; i < 2 * S::LOADS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        // Register r holds key kv0 + 8*(r/4) + 4*hh + r%4.
+        const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > r0 + coff);
+        if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool ok = key < ke && (!CAUSAL || key <= qrow + coff);
+                s[r] = ok ? s[r] : NEG_INF;
+            }
+        }
+        float mx = NEG_INF;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = xhalf_max(mx);
+        const float m_tile = mx == NEG_INF ? NEG_INF : mx * c;
+        const float m_new = fmaxf(m_run, m_tile);
+        const float m_use = m_new == NEG_INF ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m_use));
+            if (need_mask) e = s[r] == NEG_INF ? 0.f : e;
+            s[r] = e;
+            lsum += e;
+        }
+        l_run = alpha * l_run + lsum;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int row = 8 * (u >> 2) + 4 * hh + (u & 3);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[row * S::VS + 32 * db + l32], s[u], oacc[db], 0,
+                                                                0, 0);
+            }
+        }
+    }
+
+    // Merge.  Each wave publishes the m and l of its 32 rows; every wave
+    // then forms the row's M = max_w m_w and L = sum_w l_w 2^{m_w - M} (the
+    // same reads in the same order, so the same values), scales its own o~
+    // by 2^{m_w - M} / L and stores it; the workgroup sums the KW scaled
+    // tiles.  A row with L = 0 (no visible key) gets o = 0 and LSE = -inf.
+    const float l_tot = xhalf_sum(l_run);
+    float *own = smem + wave * S::REGION;  // this wave's K/V staging, now free
+    __builtin_amdgcn_wave_barrier();
+    if (hh == 0) {
+        own[32 * S::OS + l32] = m_run;
+        own[32 * S::OS + 32 + l32] = l_tot;
+    }
+    __syncthreads();
+    float mm = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < S::KW; ++w) mm = fmaxf(mm, smem[w * S::REGION + 32 * S::OS + l32]);
+    float ll = 0.f;
+    if (mm != NEG_INF) {
+#pragma unroll
+        for (int w = 0; w < S::KW; ++w) {
+            const float *st = smem + w * S::REGION + 32 * S::OS;
+            ll += __builtin_amdgcn_exp2f(st[l32] - mm) * st[32 + l32];  // 0 for an empty wave
+        }
+    }
+    const float wt = ll > 0.f ? __builtin_amdgcn_exp2f(m_run - mm) / ll : 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            f32x4 x;
+            x[0] = oacc[db][4 * g] * wt;
+            x[1] = oacc[db][4 * g + 1] * wt;
+            x[2] = oacc[db][4 * g + 2] * wt;
+            x[3] = oacc[db][4 * g + 3] * wt;
+            // register 4g + j holds column 32*db + 8*g + 4*hh + j of row l32
+            *reinterpret_cast<f32x4 *>(&own[l32 * S::OS + 32 * db + 8 * g + 4 * hh]) = x;
+        }
+    if (wave == 0 && hh == 0 && r0 + l32 < N)
+        lse[(size_t)bh * N + r0 + l32] = ll > 0.f ? (mm + log2f(ll)) * LN2 : NEG_INF;
+    __syncthreads();
+    // Thread t sums float4 chunks t, t + 64*KW, ... of the 32 x D output.
+    for (int f = tid; f < 32 * D / 4; f += 64 * S::KW) {
+        const int row = f / (D / 4), c4 = f % (D / 4);
+        f32x4 acc = *reinterpret_cast<const f32x4 *>(&smem[row * S::OS + 4 * c4]);
+#pragma unroll
+        for (int w = 1; w < S::KW; ++w) acc += *reinterpret_cast<const f32x4 *>(&smem[w * S::REGION + row * S::OS + 4 * c4]);
+        if (r0 + row < N) *reinterpret_cast<f32x4 *>(&o[((size_t)bh * N + r0 + row) * D + 4 * c4]) = acc;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_small_t(const AttnProblem &p, hipStream_t stream) {
+    using S = Small<D>;
+    const int nrb = (p.N + 31) / 32;
+    hipLaunchKernelGGL((attn_fwd_f32_small_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.BH * nrb)),
+                       dim3(64 * S::KW), 0, stream, static_cast<const float *>(p.q),
+                       static_cast<const float *>(p.k), static_cast<const float *>(p.v), static_cast<float *>(p.o),
+                       p.lse, p.BH, p.N, p.M, p.c, p.negate_q ? -1.f : 1.f, nrb, p.kv_len, p.H, p.causal_off);
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
     const int ntq = (p.N + BR - 1) / BR;
@@ -257,6 +484,12 @@ hipError_t launch_d(const AttnProblem &p, hipStream_t stream) {
 
 hipError_t launch_attn_f32(const AttnProblem &p, hipStream_t stream) {
     return p.d == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
+}
+
+hipError_t launch_attn_f32_small(const AttnProblem &p, hipStream_t stream) {
+    if (p.splits != 1 || p.bias != nullptr) return hipErrorInvalidValue;  // single pass, no bias
+    if (p.d == 64) return p.causal ? launch_small_t<64, true>(p, stream) : launch_small_t<64, false>(p, stream);
+    return p.causal ? launch_small_t<128, true>(p, stream) : launch_small_t<128, false>(p, stream);
 }
 
 }  // namespace osa

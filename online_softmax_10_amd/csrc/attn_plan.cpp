@@ -20,7 +20,8 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 struct Plan {
-    enum Kind { SINGLE, SPLIT, DECODE } kind;
+    // SMALL: single pass of the small fp32 kernel (keys split inside a workgroup).
+    enum Kind { SINGLE, SPLIT, DECODE, SMALL } kind;
     int splits;
     int tiles_per_split;  // in units of the chosen kernel's key tile
 };
@@ -56,6 +57,12 @@ Plan plan_for(int64_t BH, int64_t N, int64_t M, int d, bool bf16, int num_splits
     }
     const int tile = bf16 ? kBf16KeyTile : kF32KeyTile;
     const int row_tiles = ceil_div(N, 128);
+    // Small fp32 problems that cannot fill the chip with 128-row workgroups
+    // and whose keys fit at most 8 tiles per wave of the small kernel: one
+    // launch, the keys split among the waves of each 32-row workgroup.
+    if (!bf16 && !bias && num_splits == 0 && BH * row_tiles < 256 &&
+        ceil_div(M, kF32KeyTile) <= 8 * (d == 64 ? kF32SmallWaves64 : kF32SmallWaves128))
+        return Plan{Plan::SMALL, 1, 0};
     int s = num_splits;
     if (s == 0) {
         // Split only when the query tiles alone cannot fill the 256 compute
@@ -101,6 +108,7 @@ int validate_args(const void *q, const void *k, const void *v, const void *o, co
 
 MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16, bool bias = false, bool out_f32 = false) {
     if (plan.kind == Plan::DECODE) return MainKernel::DECODE;
+    if (plan.kind == Plan::SMALL) return MainKernel::F32_SMALL;
     if (!bf16) return MainKernel::F32;
     // fp32 output with a bias: the four-wave width (its partial-store form
     // fits the registers; the eight-wave one would spill).
@@ -118,6 +126,7 @@ MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16, bool 
 const char *main_kernel_name(MainKernel k) {
     switch (k) {
     case MainKernel::F32: return "attn_fwd_f32_kernel";
+    case MainKernel::F32_SMALL: return "attn_fwd_f32_small_kernel";
     case MainKernel::BF16_4W: return "attn_fwd_bf16_kernel";
     case MainKernel::BF16_8W: return "attn_fwd_bf16_w8_kernel";
     case MainKernel::DECODE: return "attn_decode_kernel";
@@ -180,13 +189,15 @@ int plan_attn(const void *q, const void *k, const void *v, void *o, float *lse, 
     p.out_f32 = dtype == ATTN_BF16_OUT_F32;
 
     const Plan plan = plan_for(BH, N, M, d, bf16, num_splits, p.bias != nullptr);
-    const int64_t blocks = plan.kind == Plan::DECODE ? BH * plan.splits : BH * ceil_div(N, 128) * plan.splits;
+    const int64_t blocks = plan.kind == Plan::DECODE  ? BH * plan.splits
+                           : plan.kind == Plan::SMALL ? BH * ceil_div(N, 32)
+                                                      : BH * ceil_div(N, 128) * plan.splits;
     if (blocks > kMaxBlocks) return ATTN_ERR_OVERFLOW;
     out->kernel = main_kernel(plan, BH, N, bf16, p.bias != nullptr, p.out_f32);
     out->bf16 = bf16;
     p.splits = plan.splits;
     p.tiles_per_split = plan.tiles_per_split;
-    out->split = plan.kind != Plan::SINGLE;
+    out->split = plan.kind == Plan::SPLIT || plan.kind == Plan::DECODE;
     out->workspace_bytes = 0;
     if (!out->split) {
         p.tiles_per_split = ceil_div(M, bf16 ? kBf16KeyTile : kF32KeyTile);

@@ -21,6 +21,9 @@ hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream);
 // Eight-wave bf16 kernel: 256 query rows per workgroup, single pass only.
 hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnProblem &p, hipStream_t stream);
+// fp32, small problems: one workgroup per 32-row block, keys split over its
+// waves and merged in LDS; single pass, no bias.
+hipError_t launch_attn_f32_small(const AttnProblem &p, hipStream_t stream);
 // Few queries per head (N <= kDecodeMaxQueries), bf16 or fp32 inputs, always
 // writes partials (p.splits >= 1).
 hipError_t launch_attn_decode(const AttnProblem &p, bool bf16, hipStream_t stream);

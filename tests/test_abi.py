@@ -153,7 +153,12 @@ def test_plan_kernel_choice():
     assert osa.plan(4, 8, 1024, 1024, 64) == ("attn_fwd_bf16_kernel", 1)
     name, s = osa.plan(32, 32, 1, 8192, 128)
     assert name == "attn_decode_kernel" and 1 <= s <= osa.ATTN_MAX_SPLITS
-    assert osa.plan(1, 1, 256, 256, 64, "f32")[0] == "attn_fwd_f32_kernel"
+    # the fp32 workload: one launch, keys split among the waves of each 32-row workgroup
+    assert osa.plan(1, 1, 256, 256, 64, "f32") == ("attn_fwd_f32_small_kernel", 1)
+    assert osa.plan(1, 1, 256, 256, 64, "f32", num_splits=1) == ("attn_fwd_f32_kernel", 1)
+    assert osa.plan(1, 1, 100, 5000, 64, "f32")[0] == "attn_fwd_f32_kernel"  # long key ranges: split partials
+    assert osa.plan(1, 1, 256, 256, 128, "f32") == ("attn_fwd_f32_small_kernel", 1)
+    assert osa.plan(1, 1, 256, 1025, 128, "f32")[0] == "attn_fwd_f32_kernel"
     # Few query tiles and a long key range: split partials, merged afterwards.
     name, s = osa.plan(1, 1, 100, 8000, 64)
     assert name == "attn_fwd_bf16_kernel" and s > 1
@@ -164,7 +169,7 @@ def test_plan_kernel_choice():
     assert osa.plan(2, 4, 512, 512, 64) == ("attn_fwd_bf16_kernel", 1)
     assert osa.plan(1, 16, 1024, 1024, 128) == ("attn_fwd_bf16_kernel", 1)
     assert osa.plan(1, 2, 2048, 2048, 64) == ("attn_fwd_bf16_kernel", 1)
-    assert osa.plan(1, 1, 256, 256, 64, "f32")[1] > 1
+    assert osa.plan(1, 1, 256, 256, 64, "f32", num_splits=2) == ("attn_fwd_f32_kernel", 2)
     # An explicit single pass on a small problem takes the four-wave kernel;
     # the eight-wave kernel never writes partials.
     assert osa.plan(1, 1, 100, 5000, 64, num_splits=1) == ("attn_fwd_bf16_kernel", 1)
