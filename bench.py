@@ -40,9 +40,10 @@ import seeded_inputs as si  # noqa: E402
 
 PEAKS_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
 HBM_PEAK_GBS = 8000.0
-# Device code of the attention kernels: the stamp of the committed traffic
-# figures (host-side planning is covered by the kernel name they record).
-KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16_common.h", "attn_f32.hip", "attn_decode.hip"]
+# Device code of the bf16 attention kernels, whose traffic the committed
+# figures record: their stamp (the planning is covered by the kernel name
+# each figure records).
+KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16_common.h"]
 
 
 def err(msg: str) -> None:
