@@ -40,21 +40,28 @@ import seeded_inputs as si  # noqa: E402
 
 PEAKS_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
 HBM_PEAK_GBS = 8000.0
-# Device code of the bf16 attention kernels, whose traffic the committed
-# figures record: their stamp (the planning is covered by the kernel name
+# Device code of each attention kernel whose traffic a committed figure may
+# record: the figure's stamp (the planning is covered by the kernel name
 # each figure records).
-KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16_common.h"]
+BF16_SOURCES = ["attn_bf16.hip", "attn_bf16_common.h"]
+KERNEL_SOURCES = {
+    "attn_fwd_bf16_w8_kernel": BF16_SOURCES,
+    "attn_fwd_bf16_kernel": BF16_SOURCES,
+    "attn_decode_kernel": ["attn_decode.hip"],
+    "attn_fwd_f32_small_kernel": ["attn_f32.hip"],
+    "attn_fwd_f32_kernel": ["attn_f32.hip"],
+}
 
 
 def err(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the attention sources' code: // comments, trailing blanks and
-    empty lines are dropped, so a comment-only edit keeps the stamp."""
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the device sources of `kernel`: // comments, trailing blanks
+    and empty lines are dropped, so a comment-only edit keeps the stamp."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "online_softmax_10_amd", "csrc", name), encoding="utf-8") as f:
             for line in f:
                 code = line.split("//", 1)[0].rstrip()
@@ -71,7 +78,7 @@ def load_traffic(workload: str, kernel: str, path: str = ""):
         return None
     with open(path, encoding="utf-8") as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("kernel") != kernel:
+    if t.get("kernel") != kernel or t.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -82,7 +89,7 @@ COPY_MIB = 512  # size of the plain copy that calibrates the byte counters
 def counter_commands(wl: str, out_dir: str) -> list:
     """The four rocprofv3 counter runs (from the repository root, results
     under out_dir) that --traffic-from-counters reads back."""
-    run = f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --trials 0 --workload {wl}"
+    run = f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --trials 0 --no-gemm-ceiling --workload {wl}"
     cal = f"python3 bench.py --calibrate-copy {COPY_MIB} --steps 3"
     pmc = "timeout -s KILL 120 rocprofv3 --pmc"
     return [f"{pmc} FETCH_SIZE --output-format csv -d {out_dir}/pmc_fetch_{wl} -o run -- {run}",
@@ -125,7 +132,7 @@ def traffic_from_counters(wl: str, kernel: str, out_dir: str, dest: str = "") ->
     out = {
         "workload": wl,
         "kernel": kernel,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(kernel),
         "fetch_kib_per_dispatch": round(fk, 1),
         "write_kib_per_dispatch": round(wk, 1),
         "copy_calibration": {"bytes": copy_kib * 1024, "fetch_factor": round(ff, 4), "write_factor": round(fw, 4)},
@@ -290,26 +297,32 @@ def bench_softmax(args, torch, osa) -> int:
     return 0
 
 
-def bench_gemm(args, torch) -> int:
-    """torch.mm (hipBLASLt) on bf16 N x N matrices of N(0,1) values: the dense
-    matrix-core rate the chip sustains on random data, timed like attention."""
-    n = args.gemm_ceiling
-    g = torch.Generator(device="cuda").manual_seed(args.seed)
+def time_gemm(torch, n: int, steps: int, warmup: int, seed: int):
+    """torch.mm (hipBLASLt) on bf16 n x n matrices of N(0,1) values, timed like
+    attention (one timed region of `steps` launches): (ms per launch, TFLOP/s)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
     a = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     b = torch.randn((n, n), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
     c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         torch.mm(a, b, out=c)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         torch.mm(a, b, out=c)
     t1.record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    ms = t0.elapsed_time(t1) / steps
+    del a, b, c
+    return ms, 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
+def bench_gemm(args, torch) -> int:
+    """The dense matrix-core rate the chip sustains on random data."""
+    n = args.gemm_ceiling
+    ms, tflops = time_gemm(torch, n, args.steps, args.warmup, args.seed)
     print(json.dumps({"metric": "bf16 GEMM TFLOP/s (torch.mm, vendor library)", "value": round(tflops, 1),
                       "unit": "TFLOP/s", "n": n, "steps": args.steps, "warmup": args.warmup,
                       "ms_per_step": round(ms, 4), "pct_of_bf16_peak": round(100 * tflops / PEAKS_TFLOPS["bf16"], 2),
@@ -407,6 +420,8 @@ def main() -> int:
     ap.add_argument("--gemm-ceiling", type=int, default=0, metavar="N",
                     help="only time torch.mm on N x N bf16 matrices of N(0,1) values (the vendor GEMM): the "
                          "matrix-core rate this chip sustains on random data, for comparison with attention")
+    ap.add_argument("--no-gemm-ceiling", action="store_true",
+                    help="skip the vendor bf16 GEMM timed after a bf16 attention run (bf16_gemm_ceiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--traffic-from-counters", default="", metavar="DIR",
@@ -545,21 +560,43 @@ def main() -> int:
             kernel = "attn_fwd_bf16_w8_bias_kernel" if kernel == "attn_fwd_bf16_w8_kernel" else "attn_fwd_bf16_bias_kernel"
         abytes += w.N * w.M * 4  # the broadcast bias, read once
     achieved = w.flops / (launch_ms * 1e-3) / 1e12
-    peak = PEAKS_TFLOPS[w.dtype]
+    gbs = abytes / (launch_ms * 1e-3) / 1e9
+    # The decode kernel reads each key and value once for a handful of
+    # queries: bound by HBM, not by the matrix cores.
+    hbm_bound = kernel == "attn_decode_kernel"
+    peak = HBM_PEAK_GBS if hbm_bound else PEAKS_TFLOPS[w.dtype]
     roofline = {
-        "bound": "mfma",
-        "achieved": round(achieved, 2),
+        "bound": "hbm" if hbm_bound else "mfma",
+        "achieved": round(gbs if hbm_bound else achieved, 2),
         "peak": peak,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / peak, 4),
-        "traffic": load_traffic(w.name, kernel) if splits == 1 and not args.bias else None,
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
+        "frac": round((gbs if hbm_bound else achieved) / peak, 4),
+        # HBM bytes per launch of the kernel named, from the committed
+        # counter runs (a split call also runs the small merge kernel).
+        "traffic": load_traffic(w.name, kernel) if (splits == 1 or hbm_bound) and not args.bias else None,
         "kernel": kernel,
         "splits": splits,
         "launch_us": round(launch_ms * 1e3, 2),
         "launch_timing": "per-launch event pairs" if args.launch_events else "timed region / steps",
+        "achieved_from": ("algorithmic work of one call / launch_us" +
+                          ("" if args.launch_events else
+                           ", launch_us = the timed region / steps: the gaps between launches count against "
+                           "the kernel (the rocprofv3 kernel trace gives the kernel alone)")),
         "algorithmic_bytes": abytes,
-        "hbm_gbs_algorithmic": round(abytes / (launch_ms * 1e-3) / 1e9, 1),
+        "hbm_gbs_algorithmic": round(gbs, 1),
     }
+    if hbm_bound:
+        roofline["tflops"] = round(achieved, 2)
+
+    # The vendor bf16 GEMM on random data in the same process, after the
+    # attention timing: the matrix-core rate this chip sustains, beside the
+    # share of the published peak.
+    gemm_ceiling = None
+    if w.dtype == "bf16" and not args.no_gemm_ceiling and args.order == "q_outer" and not hbm_bound:
+        gms, gtf = time_gemm(torch, 8192, 20, 5, args.seed)
+        gemm_ceiling = {"what": "torch.mm bf16 8192^3, N(0,1) operands (hipBLASLt), 20 launches after 5",
+                        "tflops": round(gtf, 1), "pct_of_bf16_peak": round(100.0 * gtf / PEAKS_TFLOPS["bf16"], 2),
+                        "value_over_ceiling": round(value / gtf, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -588,6 +625,7 @@ def main() -> int:
                                   if args.bias else ""),
                    "B": w.B, "H": w.H, "N": w.N, "M": w.M, "d": w.d, "causal": w.causal},
         "pct_of_bf16_peak": round(100.0 * value / PEAKS_TFLOPS["bf16"], 2),
+        "bf16_gemm_ceiling": gemm_ceiling,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -62,7 +62,7 @@ def test_traffic_from_counters(tmp_path):
     assert t["fetch_kib_per_dispatch"] == 100.0 and t["write_kib_per_dispatch"] == 50.0
     assert t["hbm_bytes_per_launch"] == (100 * 2 + 50 * 1) * 1024
     with open(dest, encoding="utf-8") as f:
-        assert json.load(f)["kernel_source_hash"] == bench.kernel_source_hash()
+        assert json.load(f)["kernel_source_hash"] == bench.kernel_source_hash(k)
     # Read back only for the same kernel and the same kernel sources.
     assert bench.load_traffic("c3", k, dest) == t["hbm_bytes_per_launch"]
     assert bench.load_traffic("c3", "attn_fwd_bf16_kernel", dest) is None
@@ -75,22 +75,27 @@ def test_traffic_from_counters(tmp_path):
 def test_source_stamp_ignores_comments(tmp_path, monkeypatch):
     src = tmp_path / "online_softmax_10_amd" / "csrc"
     src.mkdir(parents=True)
-    for name in bench.KERNEL_SOURCES:
+    names = sorted({n for srcs in bench.KERNEL_SOURCES.values() for n in srcs})
+    for name in names:
         (src / name).write_text("int a = 1;  // one\n\n// note\nint b = 2;\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    h0 = bench.kernel_source_hash()
-    (src / bench.KERNEL_SOURCES[0]).write_text("int a = 1;  // another note\n// more\nint b = 2;   \n")
-    assert bench.kernel_source_hash() == h0
-    (src / bench.KERNEL_SOURCES[0]).write_text("int a = 1;\nint b = 3;\n")
-    assert bench.kernel_source_hash() != h0
+    k = "attn_fwd_bf16_w8_kernel"
+    h0 = {kern: bench.kernel_source_hash(kern) for kern in bench.KERNEL_SOURCES}
+    first = bench.KERNEL_SOURCES[k][0]
+    (src / first).write_text("int a = 1;  // another note\n// more\nint b = 2;   \n")
+    assert bench.kernel_source_hash(k) == h0[k]
+    (src / first).write_text("int a = 1;\nint b = 3;\n")
+    assert bench.kernel_source_hash(k) != h0[k]
+    # a kernel whose sources did not change keeps its stamp
+    assert bench.kernel_source_hash("attn_decode_kernel") == h0["attn_decode_kernel"]
 
 
 def test_committed_traffic_matches_the_sources():
     # The committed counter summaries were taken on the current kernels.
-    for wl in ("c3", "c4"):
+    for wl in ("c3", "c4", "c5"):
         path = os.path.join(ROOT, "profiles", f"traffic_attn_fwd_{wl}.json")
         with open(path, encoding="utf-8") as f:
             t = json.load(f)
-        if t["kernel_source_hash"] != bench.kernel_source_hash():
+        if t["kernel_source_hash"] != bench.kernel_source_hash(t["kernel"]):
             pytest.fail(f"{path} was taken on other kernel sources; re-take the counter runs it lists")
         assert t["hbm_bytes_per_launch"] >= bench.algorithmic_bytes(si.WORKLOADS[wl])
