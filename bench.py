@@ -420,6 +420,9 @@ def main() -> int:
     ap.add_argument("--gemm-ceiling", type=int, default=0, metavar="N",
                     help="only time torch.mm on N x N bf16 matrices of N(0,1) values (the vendor GEMM): the "
                          "matrix-core rate this chip sustains on random data, for comparison with attention")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed steps in one HIP graph and replay it (the trials replay it again): "
+                         "the device's rate for launches shorter than the host's per-call work")
     ap.add_argument("--no-gemm-ceiling", action="store_true",
                     help="skip the vendor bf16 GEMM timed after a bf16 attention run (bf16_gemm_ceiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -464,6 +467,10 @@ def main() -> int:
         return bench_softmax(args, torch, osa)
     if args.xent:
         return bench_xent(args, torch, osa)
+    if args.graph and (args.order == "kv_outer" or args.launch_events or args.bias):
+        print("--graph times the single-launch attention plans only (no --order kv_outer, --launch-events or --bias).",
+              file=sys.stderr)
+        return 2
     if args.bias and args.order == "kv_outer":
         print("--bias applies to the fused (query-outer) kernels only.", file=sys.stderr)
         return 2
@@ -507,6 +514,25 @@ def main() -> int:
     # duration / K (each step is one launch of the dominant kernel; any gap
     # between launches is counted, so it is an upper bound).
     stream = torch.cuda.current_stream()
+    run_steps = None
+    if args.graph and osa.plan(w.B, w.H, w.N, w.M, w.d, w.dtype)[1] != 1:
+        print("--graph times the single-launch attention plans only (this workload splits its keys).", file=sys.stderr)
+        return 2
+    if args.graph:
+        # The K steps captured once in a HIP graph and replayed: the launches
+        # go out without the host's per-call work in between (for problems
+        # whose launch is shorter than the binding's call).
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(args.steps):
+                    step()
+        stream.wait_stream(side)
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
+        run_steps = graph.replay
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] if args.launch_events else []
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] if args.launch_events else []
     t_begin = torch.cuda.Event(enable_timing=True)
@@ -514,12 +540,15 @@ def main() -> int:
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_begin.record(stream)
-    for i in range(args.steps):
-        if args.launch_events:
-            starts[i].record(stream)
-        step()
-        if args.launch_events:
-            ends[i].record(stream)
+    if run_steps is not None:
+        run_steps()
+    else:
+        for i in range(args.steps):
+            if args.launch_events:
+                starts[i].record(stream)
+            step()
+            if args.launch_events:
+                ends[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -534,8 +563,11 @@ def main() -> int:
         for _ in range(args.trials):
             torch.cuda.synchronize()
             ta.record(stream)
-            for _ in range(args.steps):
-                step()
+            if run_steps is not None:
+                run_steps()
+            else:
+                for _ in range(args.steps):
+                    step()
             tb.record(stream)
             torch.cuda.synchronize()
             trial_us.append(ta.elapsed_time(tb) / args.steps * 1e3)
@@ -577,7 +609,8 @@ def main() -> int:
         "kernel": kernel,
         "splits": splits,
         "launch_us": round(launch_ms * 1e3, 2),
-        "launch_timing": "per-launch event pairs" if args.launch_events else "timed region / steps",
+        "launch_timing": ("per-launch event pairs" if args.launch_events else
+                          "timed region / steps" + (", the steps replayed from one HIP graph" if args.graph else "")),
         "achieved_from": ("algorithmic work of one call / launch_us" +
                           ("" if args.launch_events else
                            ", launch_us = the timed region / steps: the gaps between launches count against "

@@ -252,25 +252,46 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_f32_kernel(
         }
 }
 
-// Small problems: one workgroup per 32-row query block, its KW waves each
-// taking every KW-th key tile (a split over keys inside the workgroup; tiles
-// interleaved so causal ranges share out evenly), with K and V staged in each
-// wave's own LDS region.  Each wave keeps the running max, sum and
+// Small problems: one workgroup per 16-row query block, its KW waves each
+// taking every KW-th 32-key tile (a split over keys inside the workgroup;
+// tiles interleaved so causal ranges share out evenly), with K and V staged
+// in each wave's own LDS region.  Each wave keeps the running max, sum and
 // unnormalised accumulator of its tiles; at the end the waves' states are
 // merged in LDS with the same rule as any two blocks of the recurrence
 // (L = sum_w l_w 2^{m_w - M}, O = sum_w o~_w 2^{m_w - M} / L, M the largest
 // m_w): "从原始Softmax到在线Softmax" page, the merge of two (m, l, o~)
 // states.  One launch, no workspace.  No bias (the four-wave kernel above
 // takes those).
+//
+// Products on v_mfma_f32_16x16x4_f32 (A 16x4, B 4x16, one value per lane per
+// operand; result register r of lane l is row 4*(l/16) + r, column l%16).
+// Scores are computed transposed, S^T = K Q^T, 16 keys x 16 queries per
+// block, so lane l owns query l%16 and keys 4*(l/16) + r of the block.  The
+// feature index of product step kk for lane group g = l/16 is 16*g + kk, so a
+// lane reads 16 consecutive floats of its key row (and of its query row).
+// P^T feeds O^T += V^T P^T straight from the score registers: step r of a
+// key block takes key 4*g + r in lane group g, which is register r.
 template <int D>
 struct Small {
     static constexpr int KW = D == 64 ? kF32SmallWaves64 : kF32SmallWaves128;  // waves per workgroup
-    static constexpr int KS = D + 2, VS = D + 8;         // LDS row strides (floats), as above
+    static constexpr int KS = D + 4, VS = D + 4;         // LDS row strides (floats): conflict-free reads
     static constexpr int REGION = BC * (KS + VS);        // floats per wave: a K tile and a V tile
     static constexpr int LOADS = BC * D / 4 / 64;        // float4 chunks per lane per tile (K and V each)
     static constexpr int OS = D + 4;                     // row stride (floats) of a wave's scaled o~ in the merge
-    static_assert(REGION >= 32 * OS + 64, "the merge state fits a wave's region");
+    static_assert(REGION >= 16 * OS + 32, "the merge state fits a wave's region");
 };
+
+// Max and sum over the four 16-lane rows of a wave (the keys of one query).
+__device__ __forceinline__ float rows4_max(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    return xhalf_max(x);
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    return xhalf_sum(x);
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * Small<D>::KW, 1) void attn_fwd_f32_small_kernel(
@@ -282,19 +303,19 @@ __global__ __launch_bounds__(64 * Small<D>::KW, 1) void attn_fwd_f32_small_kerne
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int l32 = lane & 31;
-    const int hh = lane >> 5;
+    const int l16 = lane & 15;  // this lane's query in the block
+    const int g = lane >> 4;    // lane group: keys 4g..4g+3 of a 16-key block, features 16g..16g+15
     float *Ks = smem + wave * S::REGION;
     float *Vs = Ks + BC * S::KS;
 
-    // Workgroup -> (head, 32-row block); the longest causal blocks first.
+    // Workgroup -> (head, 16-row block); the longest causal blocks first.
     const int bh = blockIdx.x % BH;
     const int rb = nrb - 1 - blockIdx.x / BH;
-    const int r0 = rb * 32;
-    const int qrow = r0 + l32;
+    const int r0 = rb * 16;
+    const int qrow = r0 + l16;
     int ke = M;
     if (kv_len != nullptr) ke = min(ke, max(kv_len[bh / H], 0));
-    if (CAUSAL) ke = min(ke, r0 + 32 + coff);
+    if (CAUSAL) ke = min(ke, r0 + 16 + coff);
     const int ntiles = ke > 0 ? (ke + BC - 1) / BC : 0;
 
     const float *qh = q + (size_t)bh * N * D;
@@ -321,12 +342,28 @@ __global__ __launch_bounds__(64 * Small<D>::KW, 1) void attn_fwd_f32_small_kerne
         }
     };
     load_tile(wave);
-    float qop[D / 2];
-    load_q_operand<D>(qh, N, qrow, hh, qsign, qop);
-
-    f32x16 oacc[D / 32];
+    // Q operand: lane (query l16, group g) holds q[qrow][16g + kk], kk < 16,
+    // per D/64 feature chunks, times qsign (0 for a row past N; rows past N
+    // read row N - 1).
+    float qop[D / 4];
+    {
+        const float *qr = qh + (size_t)min(qrow, N - 1) * D;
+        const float f = qrow < N ? qsign : 0.f;
+        f32x4 x[D / 16];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+        for (int ch = 0; ch < D / 64; ++ch)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[4 * ch + j] = *reinterpret_cast<const f32x4 *>(qr + 64 * ch + 16 * g + 4 * j);
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qop[4 * i + e] = x[i][e] * f;
+    }
+
+    // O^T accumulator: block db, register r is feature 16*db + 4g + r of query l16.
+    f32x4 oacc[D / 16];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{};
     float m_run = NEG_INF;
     float l_run = 0.f;
 
@@ -337,11 +374,7 @@ __global__ __launch_bounds__(64 * Small<D>::KW, 1) void attn_fwd_f32_small_kerne
         for (int i = 0; i < S::LOADS; ++i) {
             const int id = lane + 64 * i;
             const int row = id / (D / 4), c4 = id % (D / 4);
-            float *kd = &Ks[row * S::KS + 4 * c4];
-            kd[0] = kr[i][0];
-            kd[1] = kr[i][1];
-            kd[2] = kr[i][2];
-            kd[3] = kr[i][3];
+            *reinterpret_cast<f32x4 *>(&Ks[row * S::KS + 4 * c4]) = kr[i];
             *reinterpret_cast<f32x4 *>(&Vs[row * S::VS + 4 * c4]) = vr[i];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -349,30 +382,47 @@ __global__ __launch_bounds__(64 * Small<D>::KW, 1) void attn_fwd_f32_small_kerne
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         load_tile(t + S::KW);  // zeros once past the last tile
-        f32x16 s = f32x16{};
-        const float *krow = &Ks[l32 * S::KS + hh];
+        // S^T for the tile's two 16-key blocks.
+        f32x4 s[2];
 #pragma unroll
-        for (int kk = 0; kk < D / 2; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * kk], qop[kk], s, 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x4{};
+            const float *krow = &Ks[(16 * kb + l16) * S::KS + 16 * g];
+#pragma unroll
+            for (int ch = 0; ch < D / 64; ++ch) {
+                f32x4 kop[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kop[j] = *reinterpret_cast<const f32x4 *>(krow + 64 * ch + 4 * j);
+#pragma unroll
+                for (int kk = 0; kk < 16; ++kk)
+                    s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kop[kk / 4][kk % 4], qop[16 * ch + kk], s[kb], 0, 0,
+                                                                 0);
+            }
+        }
         // The next tile's loads go out one per two products of this tile.
 #pragma unroll
         for (int i = 0; i < 2 * S::LOADS; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-        // Register r holds key kv0 + 8*(r/4) + 4*hh + r%4.
+        // Register r of block kb holds key kv0 + 16*kb + 4g + r.
         const bool need_mask = (kv0 + BC > ke) || (CAUSAL && kv0 + BC - 1 > r0 + coff);
         if (need_mask) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool ok = key < ke && (!CAUSAL || key <= qrow + coff);
-                s[r] = ok ? s[r] : NEG_INF;
-            }
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = kv0 + 16 * kb + 4 * g + r;
+                    const bool ok = key < ke && (!CAUSAL || key <= qrow + coff);
+                    s[kb][r] = ok ? s[kb][r] : NEG_INF;
+                }
         }
         float mx = NEG_INF;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = xhalf_max(mx);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = rows4_max(mx);
         const float m_tile = mx == NEG_INF ? NEG_INF : mx * c;
         const float m_new = fmaxf(m_run, m_tile);
         const float m_use = m_new == NEG_INF ? 0.f : m_new;
@@ -380,68 +430,61 @@ __global__ __launch_bounds__(64 * Small<D>::KW, 1) void attn_fwd_f32_small_kerne
         m_run = m_new;
         float lsum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m_use));
-            if (need_mask) e = s[r] == NEG_INF ? 0.f : e;
-            s[r] = e;
-            lsum += e;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_use));
+                if (need_mask) e = s[kb][r] == NEG_INF ? 0.f : e;
+                s[kb][r] = e;
+                lsum += e;
+            }
         l_run = alpha * l_run + lsum;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int row = 8 * (u >> 2) + 4 * hh + (u & 3);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[row * S::VS + 32 * db + l32], s[u], oacc[db], 0,
-                                                                0, 0);
+            for (int r = 0; r < 4; ++r) {
+                const float *vrow = &Vs[(16 * kb + 4 * g + r) * S::VS + l16];
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * db], s[kb][r], oacc[db], 0, 0, 0);
             }
-        }
     }
 
-    // Merge.  Each wave publishes the m and l of its 32 rows; every wave
+    // Merge.  Each wave publishes the m and l of its 16 rows; every wave
     // then forms the row's M = max_w m_w and L = sum_w l_w 2^{m_w - M} (the
     // same reads in the same order, so the same values), scales its own o~
     // by 2^{m_w - M} / L and stores it; the workgroup sums the KW scaled
     // tiles.  A row with L = 0 (no visible key) gets o = 0 and LSE = -inf.
-    const float l_tot = xhalf_sum(l_run);
+    const float l_tot = rows4_sum(l_run);
     float *own = smem + wave * S::REGION;  // this wave's K/V staging, now free
     __builtin_amdgcn_wave_barrier();
-    if (hh == 0) {
-        own[32 * S::OS + l32] = m_run;
-        own[32 * S::OS + 32 + l32] = l_tot;
+    if (g == 0) {
+        own[16 * S::OS + l16] = m_run;
+        own[16 * S::OS + 16 + l16] = l_tot;
     }
     __syncthreads();
     float mm = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < S::KW; ++w) mm = fmaxf(mm, smem[w * S::REGION + 32 * S::OS + l32]);
+    for (int w = 0; w < S::KW; ++w) mm = fmaxf(mm, smem[w * S::REGION + 16 * S::OS + l16]);
     float ll = 0.f;
     if (mm != NEG_INF) {
 #pragma unroll
         for (int w = 0; w < S::KW; ++w) {
-            const float *st = smem + w * S::REGION + 32 * S::OS;
-            ll += __builtin_amdgcn_exp2f(st[l32] - mm) * st[32 + l32];  // 0 for an empty wave
+            const float *st = smem + w * S::REGION + 16 * S::OS;
+            ll += __builtin_amdgcn_exp2f(st[l16] - mm) * st[16 + l16];  // 0 for an empty wave
         }
     }
     const float wt = ll > 0.f ? __builtin_amdgcn_exp2f(m_run - mm) / ll : 0.f;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            f32x4 x;
-            x[0] = oacc[db][4 * g] * wt;
-            x[1] = oacc[db][4 * g + 1] * wt;
-            x[2] = oacc[db][4 * g + 2] * wt;
-            x[3] = oacc[db][4 * g + 3] * wt;
-            // register 4g + j holds column 32*db + 8*g + 4*hh + j of row l32
-            *reinterpret_cast<f32x4 *>(&own[l32 * S::OS + 32 * db + 8 * g + 4 * hh]) = x;
-        }
-    if (wave == 0 && hh == 0 && r0 + l32 < N)
-        lse[(size_t)bh * N + r0 + l32] = ll > 0.f ? (mm + log2f(ll)) * LN2 : NEG_INF;
+    for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<f32x4 *>(&own[l16 * S::OS + 16 * db + 4 * g]) = oacc[db] * wt;
+    if (wave == 0 && g == 0 && qrow < N)
+        lse[(size_t)bh * N + qrow] = ll > 0.f ? (mm + log2f(ll)) * LN2 : NEG_INF;
     __syncthreads();
-    // Thread t sums float4 chunks t, t + 64*KW, ... of the 32 x D output.
-    for (int f = tid; f < 32 * D / 4; f += 64 * S::KW) {
+    // Thread t sums float4 chunks t, t + 64*KW, ... of the 16 x D output.
+    for (int f = tid; f < 16 * D / 4; f += 64 * S::KW) {
         const int row = f / (D / 4), c4 = f % (D / 4);
         f32x4 acc = *reinterpret_cast<const f32x4 *>(&smem[row * S::OS + 4 * c4]);
 #pragma unroll
@@ -453,7 +496,7 @@ __global__ __launch_bounds__(64 * Small<D>::KW, 1) void attn_fwd_f32_small_kerne
 template <int D, bool CAUSAL>
 hipError_t launch_small_t(const AttnProblem &p, hipStream_t stream) {
     using S = Small<D>;
-    const int nrb = (p.N + 31) / 32;
+    const int nrb = (p.N + 15) / 16;
     hipLaunchKernelGGL((attn_fwd_f32_small_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)p.BH * nrb)),
                        dim3(64 * S::KW), 0, stream, static_cast<const float *>(p.q),
                        static_cast<const float *>(p.k), static_cast<const float *>(p.v), static_cast<float *>(p.o),

@@ -59,7 +59,7 @@ Plan plan_for(int64_t BH, int64_t N, int64_t M, int d, bool bf16, int num_splits
     const int row_tiles = ceil_div(N, 128);
     // Small fp32 problems that cannot fill the chip with 128-row workgroups
     // and whose keys fit at most 8 tiles per wave of the small kernel: one
-    // launch, the keys split among the waves of each 32-row workgroup.
+    // launch, the keys split among the waves of each 16-row workgroup.
     if (!bf16 && !bias && num_splits == 0 && BH * row_tiles < 256 &&
         ceil_div(M, kF32KeyTile) <= 8 * (d == 64 ? kF32SmallWaves64 : kF32SmallWaves128))
         return Plan{Plan::SMALL, 1, 0};
@@ -190,7 +190,7 @@ int plan_attn(const void *q, const void *k, const void *v, void *o, float *lse, 
 
     const Plan plan = plan_for(BH, N, M, d, bf16, num_splits, p.bias != nullptr);
     const int64_t blocks = plan.kind == Plan::DECODE  ? BH * plan.splits
-                           : plan.kind == Plan::SMALL ? BH * ceil_div(N, 32)
+                           : plan.kind == Plan::SMALL ? BH * ceil_div(N, 16)
                                                       : BH * ceil_div(N, 128) * plan.splits;
     if (blocks > kMaxBlocks) return ATTN_ERR_OVERFLOW;
     out->kernel = main_kernel(plan, BH, N, bf16, p.bias != nullptr, p.out_f32);

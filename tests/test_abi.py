@@ -153,7 +153,7 @@ def test_plan_kernel_choice():
     assert osa.plan(4, 8, 1024, 1024, 64) == ("attn_fwd_bf16_kernel", 1)
     name, s = osa.plan(32, 32, 1, 8192, 128)
     assert name == "attn_decode_kernel" and 1 <= s <= osa.ATTN_MAX_SPLITS
-    # the fp32 workload: one launch, keys split among the waves of each 32-row workgroup
+    # the fp32 workload: one launch, keys split among the waves of each 16-row workgroup
     assert osa.plan(1, 1, 256, 256, 64, "f32") == ("attn_fwd_f32_small_kernel", 1)
     assert osa.plan(1, 1, 256, 256, 64, "f32", num_splits=1) == ("attn_fwd_f32_kernel", 1)
     assert osa.plan(1, 1, 100, 5000, 64, "f32")[0] == "attn_fwd_f32_kernel"  # long key ranges: split partials
