@@ -326,7 +326,7 @@ __global__ __launch_bounds__(64 * Small<D>::KW, 1) void attn_fwd_f32_small_kerne
     // last) read as 0 without a branch; they are masked.  The first tile is
     // requested before Q so that the two arrive in one round trip; each later
     // tile is requested while the tile before it is in the matrix cores.
-    const int kv_bytes = max(ke, 0) * D * 4;  // ke <= M <= 1024 here
+    const int kv_bytes = max(ke, 0) * D * 4;  // ke <= M <= kF32SmallMaxKeys
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(kh), 0, kv_bytes,
                                                                          kBufferWord3);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(vh), 0, kv_bytes,
@@ -530,7 +530,8 @@ hipError_t launch_attn_f32(const AttnProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_attn_f32_small(const AttnProblem &p, hipStream_t stream) {
-    if (p.splits != 1 || p.bias != nullptr) return hipErrorInvalidValue;  // single pass, no bias
+    // Single pass, no bias, and at most kF32SmallMaxKeys keys.
+    if (p.splits != 1 || p.bias != nullptr || p.M > kF32SmallMaxKeys) return hipErrorInvalidValue;
     if (p.d == 64) return p.causal ? launch_small_t<64, true>(p, stream) : launch_small_t<64, false>(p, stream);
     return p.causal ? launch_small_t<128, true>(p, stream) : launch_small_t<128, false>(p, stream);
 }

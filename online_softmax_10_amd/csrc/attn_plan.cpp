@@ -57,11 +57,11 @@ Plan plan_for(int64_t BH, int64_t N, int64_t M, int d, bool bf16, int num_splits
     }
     const int tile = bf16 ? kBf16KeyTile : kF32KeyTile;
     const int row_tiles = ceil_div(N, 128);
-    // Small fp32 problems that cannot fill the chip with 128-row workgroups
-    // and whose keys fit at most 8 tiles per wave of the small kernel: one
-    // launch, the keys split among the waves of each 16-row workgroup.
-    if (!bf16 && !bias && num_splits == 0 && BH * row_tiles < 256 &&
-        ceil_div(M, kF32KeyTile) <= 8 * (d == 64 ? kF32SmallWaves64 : kF32SmallWaves128))
+    // Small fp32 problems that cannot fill the chip with 128-row workgroups,
+    // with at most kF32SmallMaxKeys keys (8 tiles per wave of the small
+    // kernel): one launch, the keys split among the waves of each 16-row
+    // workgroup.
+    if (!bf16 && !bias && num_splits == 0 && BH * row_tiles < 256 && M <= kF32SmallMaxKeys)
         return Plan{Plan::SMALL, 1, 0};
     int s = num_splits;
     if (s == 0) {

@@ -45,6 +45,7 @@ constexpr int kDecodeMaxQueries = 4;
 constexpr int kBf16WideRows = 256;  // query rows per workgroup of the eight-wave kernel
 constexpr int kF32SmallWaves64 = 4;  // waves per workgroup of the small fp32 kernel at d = 64
 constexpr int kF32SmallWaves128 = 4; // ... and at d = 128
+constexpr int kF32SmallMaxKeys = 1024;  // keys the small fp32 kernel takes (its buffer offsets are 32-bit)
 
 // The kernel that carries the attention itself (the split paths add the
 // merge kernel).
