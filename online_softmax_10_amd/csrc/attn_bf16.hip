@@ -82,6 +82,12 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     // none with a bias, whose runs are added during the first half of the
     // P.V phase.
     constexpr int EARLY = BIAS ? 0 : 4;
+    // The four-wave width at d = 64 (one wave per SIMD where it runs alone,
+    // as on 4x8x1024^2) reads the first V operands of the P.V phase at the
+    // start of the iteration: eight more registers live through the score
+    // phase, which it has to spare (-1.5 % per launch on 4x8x1024^2 in
+    // interleaved A/B).  At d = 128 the same move spills in the key loop.
+    constexpr bool EARLY_V = NW == 4 && D == 64;
     uint32_t popw[BC / 16][4];
     float lsum_early = 0.f;
     __shared__ __attribute__((aligned(1024))) char lds_k0[T::BYTES];
@@ -163,6 +169,14 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
             kop[0] = wt.kread(ks_next, 0);
             kop[1] = wt.kread(ks_next, 1);
         }
+        // V(j) landed with the barrier too: where the registers allow (EARLY_V),
+        // the first two V operands are read now, so that the P.V phase does
+        // not start on an LDS round trip.
+        bf16x8 vop[3];
+        if constexpr (EARLY_V) {
+            vop[0] = wt.vread(vs_cur, 0);
+            vop[1] = wt.vread(vs_cur, 1);
+        }
         fence();
 #pragma unroll
         for (int slot = 0; slot < SLOTS; ++slot) {
@@ -199,9 +213,10 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         wt.l_run = alpha * wt.l_run + lsum;
         const float sh = wt.shift_base();  // for tile j+1's scores
 
-        bf16x8 vop[3];
-        vop[0] = wt.vread(vs_cur, 0);
-        vop[1] = wt.vread(vs_cur, 1);
+        if constexpr (!EARLY_V) {
+            vop[0] = wt.vread(vs_cur, 0);
+            vop[1] = wt.vread(vs_cur, 1);
+        }
         // The next tile's scores are masked first (its early pairs are formed
         // below); a masked -inf stays -inf when shifted.
         if constexpr (FULL && !MASK_LATE) wt.mask(kb + (j + 1) * BC, ke, s_nxt);
