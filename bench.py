@@ -429,6 +429,8 @@ def main() -> int:
                          "the device's rate for launches shorter than the host's per-call work")
     ap.add_argument("--no-gemm-ceiling", action="store_true",
                     help="skip the vendor bf16 GEMM timed after a bf16 attention run (bf16_gemm_ceiling)")
+    ap.add_argument("--copy-rate", type=int, default=0, metavar="MIB",
+                    help="only time torch's device copy of MIB MiB (read + write GB/s): the rate a plain copy reaches")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--traffic-from-counters", default="", metavar="DIR",
@@ -464,6 +466,29 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": args.steps}), flush=True)
+        return 0
+    if args.copy_rate:
+        # torch's device-to-device copy (the vendor's streaming kernel), timed
+        # like the kernels here: the HBM rate a plain copy reaches.
+        n = args.copy_rate * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        gbs = 2.0 * 4 * n / (ms * 1e-3) / 1e9
+        print(json.dumps({"metric": "device copy GB/s (torch copy_, read + write)", "value": round(gbs, 1),
+                          "unit": "GB/s", "bytes_read": 4 * n, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": round(ms, 4), "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}),
+              flush=True)
         return 0
     if args.gemm_ceiling:
         return bench_gemm(args, torch)
