@@ -47,6 +47,7 @@ BF16_SOURCES = ["attn_bf16.hip", "attn_bf16_common.h"]
 KERNEL_SOURCES = {
     "attn_fwd_bf16_w8_kernel": BF16_SOURCES,
     "attn_fwd_bf16_kernel": BF16_SOURCES,
+    "attn_fwd_bf16_kh_kernel": BF16_SOURCES,
     "attn_decode_kernel": ["attn_decode.hip"],
     "attn_fwd_f32_small_kernel": ["attn_f32.hip"],
     "attn_fwd_f32_kernel": ["attn_f32.hip"],

@@ -284,9 +284,9 @@ int softmax_xent(const float *x, const int64_t *labels, float *loss, float *lse,
  * launching anything (host only; needs no GPU).
  *
  * Returns the name of the kernel that computes the attention itself (one of
- * "attn_fwd_bf16_w8_kernel", "attn_fwd_bf16_kernel", "attn_fwd_f32_kernel",
- * "attn_fwd_f32_small_kernel", "attn_decode_kernel"; a static string, not to
- * be freed) and stores in
+ * "attn_fwd_bf16_w8_kernel", "attn_fwd_bf16_kh_kernel", "attn_fwd_bf16_kernel",
+ * "attn_fwd_f32_kernel", "attn_fwd_f32_small_kernel", "attn_decode_kernel"; a
+ * static string, not to be freed) and stores in
  * *splits (if splits is not NULL) the number of key splits: 1 for a single
  * pass, >= 2 when the kernel writes partials that the merge kernel combines.
  * Returns NULL (and *splits = 0) for arguments attn_fwd_splits would reject

@@ -50,7 +50,7 @@ using namespace bf16;
 // Nothing is scheduled across this point.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-template <int NW, int D, bool CAUSAL, bool SPLIT, bool BIAS>
+template <int NW, int D, bool CAUSAL, bool SPLIT, bool BIAS, int KH = 1>
 __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                           const uint16_t *__restrict__ v, uint16_t *__restrict__ o,
                                           float *__restrict__ lse, float *__restrict__ part_o,
@@ -90,14 +90,24 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     constexpr bool EARLY_V = NW == 4 && D == 64;
     uint32_t popw[BC / 16][4];
     float lsum_early = 0.f;
-    __shared__ __attribute__((aligned(1024))) char lds_k0[T::BYTES];
-    __shared__ __attribute__((aligned(1024))) char lds_k1[T::BYTES];
-    __shared__ __attribute__((aligned(1024))) char lds_v0[T::BYTES];
-    __shared__ __attribute__((aligned(1024))) char lds_v1[T::BYTES];
+    // KH = 2: the workgroup holds two sets of NW waves on the same rows, set
+    // h taking the key tiles t = 2j + h of the range, each with its own LDS
+    // stages; their states are merged at the end.
+    static_assert(KH == 1 || (KH == 2 && !BIAS), "key halves: no bias");
+    __shared__ __attribute__((aligned(1024))) char lds_k0[KH * T::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_k1[KH * T::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_v0[KH * T::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_v1[KH * T::BYTES];
 
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = KH == 1 ? 0 : wave_all / NW;    // which key half
+    const int wave = KH == 1 ? wave_all : wave_all % NW;  // wave within its half (row block)
     const int lane = tid & 63;
+    char *const k0 = lds_k0 + half * T::BYTES;
+    char *const k1 = lds_k1 + half * T::BYTES;
+    char *const v0 = lds_v0 + half * T::BYTES;
+    char *const v1 = lds_v1 + half * T::BYTES;
 
     // Workgroup -> (head, split, query tile); heads vary fastest and the
     // longest causal tiles go first.
@@ -114,7 +124,12 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     int ke = min(M, kb + tiles_per_split * BC);
     if (kv_len != nullptr) ke = min(ke, max(kv_len[bh / H], 0));
     if (CAUSAL) ke = min(ke, q0 + BR + coff);
-    const int ntiles = ke > kb ? (ke - kb + BC - 1) / BC : 0;
+    const int tiles_wg = ke > kb ? (ke - kb + BC - 1) / BC : 0;
+    // This half's tiles are t = KH*j + half (first key tkey(j)); every wave
+    // of the workgroup passes niter barriers in the key loop.
+    const int ntiles = tiles_wg > half ? (tiles_wg - half + KH - 1) / KH : 0;
+    const int niter = (tiles_wg + KH - 1) / KH;
+    auto tkey = [&](int j) { return kb + (KH * j + half) * BC; };
 
     const u32x4 krs = make_rsrc(k + (size_t)bh * M * D, (uint32_t)M * T::RB);
     const u32x4 vrs = make_rsrc(v + (size_t)bh * M * D, (uint32_t)M * T::RB);
@@ -140,7 +155,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     // This wave's share i of tile `tile` of K (or V) into an LDS stage.
     // Unsigned offsets: M * d < 2^31, so M * 2d < 2^32.
     auto load = [&](const u32x4 &rs, int tile, char *dst, int i) {
-        const int off = (int)((uint32_t)(kb + tile * BC) * T::RB + (uint32_t)ld_off[i]);
+        const int off = (int)((uint32_t)tkey(tile) * T::RB + (uint32_t)ld_off[i]);
         lds_direct_load16(rs, lds_addr(dst + (wave * LOADS + i) * 1024), off);
     };
 
@@ -160,7 +175,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         constexpr bool FULL = decltype(full)::value;
         constexpr bool LOADS_ON = decltype(loads)::value;
         wait_loads_and_barrier<0>();
-        if constexpr (MASK_LATE) wt.mask(kb + j * BC, ke, s_cur);
+        if constexpr (MASK_LATE) wt.mask(tkey(j), ke, s_cur);
         float lsum0 = 0.f, lsum1 = 0.f;
         bf16x8 kop[3];
         if constexpr (FULL) {
@@ -219,7 +234,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         }
         // The next tile's scores are masked first (its early pairs are formed
         // below); a masked -inf stays -inf when shifted.
-        if constexpr (FULL && !MASK_LATE) wt.mask(kb + (j + 1) * BC, ke, s_nxt);
+        if constexpr (FULL && !MASK_LATE) wt.mask(tkey(j + 1), ke, s_nxt);
         float le0 = 0.f, le1 = 0.f;
         fence();
 #pragma unroll
@@ -247,7 +262,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
                 }
                 if (slot == PSLOTS / 2 && bias_next) {
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    wt.bias_dma(brs, brow, kb + (j + 2) * BC, bregion);
+                    wt.bias_dma(brs, brow, tkey(j + 2), bregion);
                 }
             }
             fence();
@@ -270,26 +285,32 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         const int row_hi = min(N, row_lo + 32) - 1;
         int last_key = ke - 1;
         if (CAUSAL) last_key = min(last_key, row_hi + coff);
-        if (row_hi >= row_lo && last_key >= kb) nw = (last_key - kb) / BC + 1;
+        if (row_hi >= row_lo && last_key >= kb) {
+            const int tl = (last_key - kb) / BC;  // last tile of the range with a visible key
+            nw = tl >= half ? (tl - half) / KH + 1 : 0;
+        }
         nw = __builtin_amdgcn_readfirstlane(nw);
     }
 
 
-    if (ntiles > 0) {
+    if (niter > 0) {
         // Prologue: every stage is free, so K(0), V(0) and K(1) load together
         // (one memory latency).  S(0) needs only Q and K(0) (and tile 0's
         // bias), issued first: it is computed once they have landed, while
         // V(0) and K(1) -- the last 2 * LOADS loads of each wave -- may still
         // be on their way (the first iteration waits for them).
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) load(krs, 0, lds_k0, i);
+        for (int i = 0; i < LOADS; ++i)
+            if (ntiles > 0) load(krs, 0, k0, i);
         if constexpr (BIAS) {
             if (nw > 0) wt.bias_dma(brs, brow, kb, bregion);
         }
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            load(vrs, 0, lds_v0, i);
-            load(krs, min(1, ntiles - 1), lds_k1, i);
+            if (ntiles > 0) {
+                load(vrs, 0, v0, i);
+                load(krs, min(1, ntiles - 1), k1, i);
+            }
         }
         wait_loads_and_barrier<2 * LOADS>();
         f32x16 sa[2] = {f32x16{}, f32x16{}}, sb[2];
@@ -298,12 +319,12 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         int j = 0;
         if (nw > 0) {
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) wt.score_step(lds_k0, kk, sa);
+            for (int kk = 0; kk < D / 16; ++kk) wt.score_step(k0, kk, sa);
             {
                 // Tile 0 masked, shifted against base 0 (no shift yet) -- with
                 // a bias by adding it (landed with the prologue's wait) --,
                 // its early pairs formed.
-                if constexpr (!MASK_LATE) wt.mask(kb, ke, sa);
+                if constexpr (!MASK_LATE) wt.mask(tkey(0), ke, sa);
                 if constexpr (BIAS) {
 #pragma unroll
                     for (int t = 0; t < 8; ++t) wt.bias_apply(bregion, t, lane, sa, c, 0.f);
@@ -326,31 +347,31 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
                 // Tile 1's bias follows tile 0's.
                 if (nw > 1) {
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    wt.bias_dma(brs, brow, kb + BC, bregion);
+                    wt.bias_dma(brs, brow, tkey(1), bregion);
                 }
             }
             for (; j + 2 < nw; j += 2) {
-                iteration(Full{}, LoadsOn{}, j, true, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
-                iteration(Full{}, LoadsOn{}, j + 1, j + 3 < nw, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+                iteration(Full{}, LoadsOn{}, j, true, sa, sb, k1, k0, v0, v1);
+                iteration(Full{}, LoadsOn{}, j + 1, j + 3 < nw, sb, sa, k0, k1, v1, v0);
             }
             // This wave's last tile: loads still go on while the workgroup has more.
             if (j + 2 == nw) {
-                iteration(Full{}, LoadsOn{}, j, false, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+                iteration(Full{}, LoadsOn{}, j, false, sa, sb, k1, k0, v0, v1);
                 ++j;
-                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, false, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
-                else iteration(Last{}, LoadsOff{}, j, false, sb, sa, lds_k0, lds_k1, lds_v1, lds_v0);
+                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, false, sb, sa, k0, k1, v1, v0);
+                else iteration(Last{}, LoadsOff{}, j, false, sb, sa, k0, k1, v1, v0);
             } else {
-                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, false, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
-                else iteration(Last{}, LoadsOff{}, j, false, sa, sb, lds_k1, lds_k0, lds_v0, lds_v1);
+                if (j + 1 < ntiles) iteration(Last{}, LoadsOn{}, j, false, sa, sb, k1, k0, v0, v1);
+                else iteration(Last{}, LoadsOff{}, j, false, sa, sb, k1, k0, v0, v1);
             }
             ++j;
         }
         // Loads only, for the tiles other waves still compute.
-        for (; j < ntiles; ++j) {
+        for (; j < niter; ++j) {
             wait_loads_and_barrier<0>();
             if (j + 1 < ntiles) {
-                char *kdst = (j & 1) ? lds_k1 : lds_k0;
-                char *vdst = (j & 1) ? lds_v0 : lds_v1;
+                char *kdst = (j & 1) ? k1 : k0;
+                char *vdst = (j & 1) ? v0 : v1;
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i) {
                     load(krs, min(j + 2, ntiles - 1), kdst, i);
@@ -362,16 +383,48 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         // no LDS-direct load is in flight past this point.
     }
 
+    // The K/V stages are free once every wave is past its last tile: each
+    // wave stages its 32 output rows in its own 64 * D bytes of them.
+    constexpr int TILE = 64 * D;  // bytes of one wave's 32 x D bf16 rows
+    static_assert(TILE * ((NW + 3) / 4) <= T::BYTES, "staged rows fit the stages");
+    char *stage = (wave & 3) == 0 ? lds_k0 : (wave & 3) == 1 ? lds_k1 : (wave & 3) == 2 ? lds_v0 : lds_v1;
+    if constexpr (KH == 2) {
+        // The two halves' states of the same rows merged by the rule for two
+        // blocks ("从原始Softmax到在线Softmax" page): half 1 leaves its
+        // accumulators in its own copy of this stage and its shift and sum
+        // past the staged rows of half 0's copy; half 0 takes them in.
+        wait_loads_and_barrier<0>();
+        float *dump = reinterpret_cast<float *>(stage + T::BYTES);
+        float *ml = reinterpret_cast<float *>(stage + TILE);
+        static_assert((D / 32) * 16 * 64 * 4 <= T::BYTES && TILE + 512 <= T::BYTES, "merge state fits a stage");
+        if (half == 1) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dump[(db * 16 + r) * 64 + lane] = wt.oacc[db][r];
+            ml[lane] = wt.m_run;
+            ml[64 + lane] = wt.l_run;
+        }
+        __syncthreads();
+        if (half == 1) return;
+        const float m1 = ml[lane], l1 = ml[64 + lane];
+        const float mm = fmaxf(wt.m_run, m1);
+        const float w0 = wt.m_run == NEG_INF ? 0.f : exp2_fast(wt.m_run - mm);
+        const float w1 = m1 == NEG_INF ? 0.f : exp2_fast(m1 - mm);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) wt.oacc[db][r] = wt.oacc[db][r] * w0 + dump[(db * 16 + r) * 64 + lane] * w1;
+        wt.l_run = wt.l_run * w0 + l1 * w1;
+        wt.m_run = mm;
+    }
     if constexpr (SPLIT) {
         wt.template store<true>(N, o + (size_t)bh * N * D, lse + (size_t)bh * N,
                                 part_o + ((size_t)sp * BH + bh) * N * D, part_lse + ((size_t)sp * BH + bh) * N);
     } else {
-        // The K/V stages are free once every wave is past its last tile: each
-        // wave stages its 32 output rows in its own 64 * D bytes of them.
-        wait_loads_and_barrier<0>();
-        constexpr int TILE = 64 * D;  // bytes of one wave's 32 x D bf16 rows
-        static_assert(TILE * ((NW + 3) / 4) <= T::BYTES, "staged rows fit the stages");
-        char *stage = (wave & 3) == 0 ? lds_k0 : (wave & 3) == 1 ? lds_k1 : (wave & 3) == 2 ? lds_v0 : lds_v1;
+        // (with key halves the merge's barrier has freed the stages, and its
+        // state lies past the staged rows)
+        if constexpr (KH == 1) wait_loads_and_barrier<0>();
         wt.store_rows(N, q0 + wave * 32, o + (size_t)bh * N * D, lse + (size_t)bh * N, stage + (wave >> 2) * TILE,
                       lane);
     }
@@ -393,6 +446,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(ATTN_KERNEL_ARGS)
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_w8_kernel(ATTN_KERNEL_ARGS) {
     attn_body<8, D, CAUSAL, SPLIT, false>(ATTN_KERNEL_PASS, nullptr, 0u, 0, 0, 0);
+}
+
+// The four-wave width with the keys split between two sets of four waves on
+// the same 128 rows (eight waves, two per SIMD), for problems whose 128-row
+// workgroups would each run alone on a CU (one wave per SIMD).
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kh_kernel(ATTN_KERNEL_ARGS) {
+    attn_body<4, D, CAUSAL, SPLIT, false, 2>(ATTN_KERNEL_PASS, nullptr, 0u, 0, 0, 0);
 }
 
 // Both widths with an additive score bias (staged through 8 KiB of LDS per
@@ -458,6 +519,17 @@ hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream) {
     return p.d == 64 ? launch_d<4, 64>(p, stream) : launch_d<4, 128>(p, stream);
 }
 
+template <int D, bool CAUSAL, bool SPLIT>
+hipError_t launch_kh_t(const AttnProblem &p, hipStream_t stream) {
+    const int ntq = (p.N + 127) / 128;
+    hipLaunchKernelGGL((attn_fwd_bf16_kh_kernel<D, CAUSAL, SPLIT>), dim3((unsigned)((int64_t)p.BH * ntq)), dim3(512), 0,
+                       stream, static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                       static_cast<const uint16_t *>(p.v), static_cast<uint16_t *>(p.o), p.lse, p.part_o, p.part_lse,
+                       p.BH, p.N, p.M, p.c, p.negate_q ? 0x80008000u : 0u, ntq, 1, p.tiles_per_split, p.kv_len, p.H,
+                       p.causal_off);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream) {
     // Single pass only (a float32 o through the partial-store form, without a
     // bias): the front end never asks this width for split partials.
@@ -468,6 +540,17 @@ hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream) {
     }
     if (p.d == 64) return p.causal ? launch_t<8, 64, true, false>(p, stream) : launch_t<8, 64, false, false>(p, stream);
     return p.causal ? launch_t<8, 128, true, false>(p, stream) : launch_t<8, 128, false, false>(p, stream);
+}
+
+hipError_t launch_attn_bf16_kh(const AttnProblem &p, hipStream_t stream) {
+    // Single pass (a float32 o through the partial-store form), no bias.
+    if (p.splits != 1 || p.bias != nullptr) return hipErrorInvalidValue;
+    if (p.out_f32) {
+        if (p.d == 64) return p.causal ? launch_kh_t<64, true, true>(p, stream) : launch_kh_t<64, false, true>(p, stream);
+        return p.causal ? launch_kh_t<128, true, true>(p, stream) : launch_kh_t<128, false, true>(p, stream);
+    }
+    if (p.d == 64) return p.causal ? launch_kh_t<64, true, false>(p, stream) : launch_kh_t<64, false, false>(p, stream);
+    return p.causal ? launch_kh_t<128, true, false>(p, stream) : launch_kh_t<128, false, false>(p, stream);
 }
 
 }  // namespace osa

@@ -106,7 +106,8 @@ int validate_args(const void *q, const void *k, const void *v, const void *o, co
     return ATTN_OK;
 }
 
-MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16, bool bias = false, bool out_f32 = false) {
+MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, int64_t M, int d, bool bf16, bool bias = false,
+                       bool out_f32 = false) {
     if (plan.kind == Plan::DECODE) return MainKernel::DECODE;
     if (plan.kind == Plan::SMALL) return MainKernel::F32_SMALL;
     if (!bf16) return MainKernel::F32;
@@ -118,6 +119,15 @@ MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, bool bf16, bool 
     // a workgroup.
     if (plan.kind == Plan::SINGLE && BH * ceil_div(N, kBf16WideRows) >= 256)
         return bias ? MainKernel::BF16_8W_BIAS : MainKernel::BF16_8W;
+    // A single pass whose 128-row workgroups run one per CU (one wave per
+    // SIMD) over enough key tiles: the keys of each workgroup split between
+    // two sets of four waves, two waves per SIMD.  Measured against the
+    // four-wave width on 4x8x1024xM, d = 64: M = 384 +5.5 %, 512 +2 %, 640
+    // +1 %, 768 -1.5 %, 1024 -4 % (causal -8 %); d = 128: M = 512 +6 %, 1024
+    // -0.3 % (1x16x1024^2: -3 %, causal -4 %).
+    if (plan.kind == Plan::SINGLE && !bias && BH * ceil_div(N, 128) <= 256 &&
+        ceil_div(M, kBf16KeyTile) >= (d == 64 ? kBf16KhMinTiles64 : kBf16KhMinTiles128))
+        return MainKernel::BF16_KH;
     return bias ? MainKernel::BF16_BIAS : MainKernel::BF16_4W;
 }
 
@@ -129,6 +139,7 @@ const char *main_kernel_name(MainKernel k) {
     case MainKernel::F32_SMALL: return "attn_fwd_f32_small_kernel";
     case MainKernel::BF16_4W: return "attn_fwd_bf16_kernel";
     case MainKernel::BF16_8W: return "attn_fwd_bf16_w8_kernel";
+    case MainKernel::BF16_KH: return "attn_fwd_bf16_kh_kernel";
     case MainKernel::DECODE: return "attn_decode_kernel";
     case MainKernel::BF16_BIAS: return "attn_fwd_bf16_bias_kernel";
     case MainKernel::BF16_8W_BIAS: return "attn_fwd_bf16_w8_bias_kernel";
@@ -193,7 +204,7 @@ int plan_attn(const void *q, const void *k, const void *v, void *o, float *lse, 
                            : plan.kind == Plan::SMALL ? BH * ceil_div(N, 16)
                                                       : BH * ceil_div(N, 128) * plan.splits;
     if (blocks > kMaxBlocks) return ATTN_ERR_OVERFLOW;
-    out->kernel = main_kernel(plan, BH, N, bf16, p.bias != nullptr, p.out_f32);
+    out->kernel = main_kernel(plan, BH, N, M, d, bf16, p.bias != nullptr, p.out_f32);
     out->bf16 = bf16;
     p.splits = plan.splits;
     p.tiles_per_split = plan.tiles_per_split;
@@ -231,7 +242,7 @@ const char *attn_fwd_plan(int64_t B, int64_t H, int64_t N, int64_t M, int d, int
     const bool bf16 = dtype != ATTN_F32;
     const Plan plan = plan_for(B * H, N, M, d, bf16, num_splits);
     if (splits) *splits = plan.splits;
-    return main_kernel_name(main_kernel(plan, B * H, N, bf16, false, dtype == ATTN_BF16_OUT_F32));
+    return main_kernel_name(main_kernel(plan, B * H, N, M, d, bf16, false, dtype == ATTN_BF16_OUT_F32));
 }
 
 const char *attn_strerror(int code) {

@@ -43,13 +43,18 @@ constexpr int kF32KeyTile = 32;
 constexpr int kDecodeKeyTile = 64;
 constexpr int kDecodeMaxQueries = 4;
 constexpr int kBf16WideRows = 256;  // query rows per workgroup of the eight-wave kernel
+// 64-key tiles a workgroup needs before its keys are split in halves (d = 64,
+// d = 128): below them the second set's fixed costs (its first loads, the
+// merge) outweigh the second wave per SIMD.
+constexpr int kBf16KhMinTiles64 = 12;
+constexpr int kBf16KhMinTiles128 = 16;
 constexpr int kF32SmallWaves64 = 4;  // waves per workgroup of the small fp32 kernel at d = 64
 constexpr int kF32SmallWaves128 = 4; // ... and at d = 128
 constexpr int kF32SmallMaxKeys = 1024;  // keys the small fp32 kernel takes (its buffer offsets are 32-bit)
 
 // The kernel that carries the attention itself (the split paths add the
 // merge kernel).
-enum class MainKernel { F32, F32_SMALL, BF16_4W, BF16_8W, DECODE, BF16_BIAS, BF16_8W_BIAS };
+enum class MainKernel { F32, F32_SMALL, BF16_4W, BF16_8W, BF16_KH, DECODE, BF16_BIAS, BF16_8W_BIAS };
 const char *main_kernel_name(MainKernel k);
 
 struct PlannedCall {

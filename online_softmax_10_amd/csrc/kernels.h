@@ -20,8 +20,13 @@ void set_hip_detail(const char *what, hipError_t e);
 hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream);
 // Eight-wave bf16 kernel: 256 query rows per workgroup, single pass only.
 hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream);
+// Key-halves bf16 kernel: 128 query rows per workgroup of eight waves, the
+// key tiles alternating between two sets of four waves and merged in LDS;
+// single pass (bf16 output, or a float32 one through the partial-store form),
+// no bias.
+hipError_t launch_attn_bf16_kh(const AttnProblem &p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnProblem &p, hipStream_t stream);
-// fp32, small problems: one workgroup per 32-row block, keys split over its
+// fp32, small problems: one workgroup per 16-row block, keys split over its
 // waves and merged in LDS; single pass, no bias.
 hipError_t launch_attn_f32_small(const AttnProblem &p, hipStream_t stream);
 // Few queries per head (N <= kDecodeMaxQueries), bf16 or fp32 inputs, always

@@ -150,7 +150,16 @@ def test_plan_kernel_choice():
     assert osa.plan(1, 8, 16384, 16384, 128) == ("attn_fwd_bf16_w8_kernel", 1)
     assert osa.plan(2, 16, 4096, 4096, 64) == ("attn_fwd_bf16_w8_kernel", 1)
     assert osa.plan(2, 16, 4096, 4096, 128, dtype="bf16_out_f32") == ("attn_fwd_bf16_w8_kernel", 1)
-    assert osa.plan(4, 8, 1024, 1024, 64) == ("attn_fwd_bf16_kernel", 1)
+    # 256 workgroups of 128 rows, one per CU: the keys split between two sets of waves
+    assert osa.plan(4, 8, 1024, 1024, 64) == ("attn_fwd_bf16_kh_kernel", 1)
+    # more than 256 workgroups of 128 rows, fewer than 256 of 256 rows: four waves
+    assert osa.plan(1, 100, 384, 300, 64) == ("attn_fwd_bf16_kernel", 1)
+    # fewer than 12 (d = 64) or 16 (d = 128) key tiles: four waves
+    assert osa.plan(1, 2, 300, 960, 128) == ("attn_fwd_bf16_kernel", 1)
+    assert osa.plan(1, 2, 300, 961, 128) == ("attn_fwd_bf16_kh_kernel", 1)
+    assert osa.plan(4, 8, 1024, 704, 64) == ("attn_fwd_bf16_kernel", 1)
+    assert osa.plan(4, 8, 1024, 705, 64) == ("attn_fwd_bf16_kh_kernel", 1)
+    assert osa.plan(4, 8, 1024, 1024, 64, dtype="bf16_out_f32") == ("attn_fwd_bf16_kh_kernel", 1)
     name, s = osa.plan(32, 32, 1, 8192, 128)
     assert name == "attn_decode_kernel" and 1 <= s <= osa.ATTN_MAX_SPLITS
     # the fp32 workload: one launch, keys split among the waves of each 16-row workgroup
@@ -167,12 +176,13 @@ def test_plan_kernel_choice():
     # Few query tiles but a short key loop: the split's workspace, merge kernel
     # and host calls would cost more than they save.
     assert osa.plan(2, 4, 512, 512, 64) == ("attn_fwd_bf16_kernel", 1)
-    assert osa.plan(1, 16, 1024, 1024, 128) == ("attn_fwd_bf16_kernel", 1)
-    assert osa.plan(1, 2, 2048, 2048, 64) == ("attn_fwd_bf16_kernel", 1)
+    assert osa.plan(1, 16, 1024, 1024, 128) == ("attn_fwd_bf16_kh_kernel", 1)
+    assert osa.plan(1, 2, 2048, 2048, 64) == ("attn_fwd_bf16_kh_kernel", 1)
     assert osa.plan(1, 1, 256, 256, 64, "f32", num_splits=2) == ("attn_fwd_f32_kernel", 2)
-    # An explicit single pass on a small problem takes the four-wave kernel;
-    # the eight-wave kernel never writes partials.
-    assert osa.plan(1, 1, 100, 5000, 64, num_splits=1) == ("attn_fwd_bf16_kernel", 1)
+    # An explicit single pass on a small problem splits its keys between two
+    # sets of waves of each workgroup (no partials, no merge kernel); the
+    # eight-wave kernel never writes partials.
+    assert osa.plan(1, 1, 100, 5000, 64, num_splits=1) == ("attn_fwd_bf16_kh_kernel", 1)
     assert osa.plan(2, 16, 4096, 4096, 128, num_splits=4) == ("attn_fwd_bf16_kernel", 4)
     assert osa.plan(1, 1, 4, 8192, 128, num_splits=8) == ("attn_decode_kernel", 8)
 

@@ -309,3 +309,82 @@ def test_wide_kernel_constant_v():
     log("[gpu] V = 1, 256-row width")
     o, _ = gpu_attention(q, k, v, "bf16", w.scale, True)
     assert np.all(np.abs(o - 1.0) <= 2.0 ** -8), f"V=1 must give O=1, max dev {np.abs(o - 1).max()}"
+
+
+# ------------------------------------------------------------------ key halves and the four-wave single pass
+
+# Single-pass shapes with at most 256 workgroups of 128 rows and at least 12
+# (d = 64) or 16 (d = 128) 64-key tiles: each workgroup's key tiles alternate between two sets of four
+# waves, merged at the end.  Odd and even tile counts, ragged tails, causal
+# ranges in which the second set sees no key for the first rows, more queries
+# than keys, peaked rows.
+KEY_HALVES = [
+    si.Workload("kh", 1, 2, 300, 1000, 64, "bf16", True, "normal"),
+    si.Workload("kh", 1, 2, 300, 1000, 128, "bf16", False, "normal"),
+    si.Workload("kh", 1, 4, 129, 1025, 128, "bf16", True, "normal"),
+    si.Workload("kh", 1, 3, 200, 769, 64, "bf16", False, "normal_qk3"),
+    si.Workload("kh", 2, 1, 900, 800, 64, "bf16", True, "normal"),
+    si.Workload("kh", 2, 2, 256, 4096, 64, "bf16", True, "normal_qk3"),
+    si.Workload("kh", 1, 8, 1024, 1023, 128, "bf16", True, "normal"),
+]
+# Single-pass shapes the four-wave kernel keeps: more than 256 workgroups of
+# 128 rows but fewer than 256 of 256 rows, or fewer key tiles.
+FOUR_WAVE = [
+    si.Workload("w4", 1, 100, 384, 300, 64, "bf16", True, "normal"),
+    si.Workload("w4", 1, 100, 300, 257, 128, "bf16", False, "normal"),
+    si.Workload("w4", 1, 2, 300, 960, 128, "bf16", True, "normal"),
+    si.Workload("w4", 2, 4, 500, 704, 64, "bf16", False, "normal"),
+]
+
+
+def _ids(ws):
+    return [f"{w.B}x{w.H}x{w.N}x{w.M}d{w.d}{'c' if w.causal else ''}{w.dist}" for w in ws]
+
+
+@pytest.mark.parametrize("w", KEY_HALVES, ids=_ids(KEY_HALVES))
+def test_key_halves_shapes(w):
+    import online_softmax_10_amd as osa
+
+    assert osa.plan(w.B, w.H, w.N, w.M, w.d, w.dtype) == ("attn_fwd_bf16_kh_kernel", 1)
+    check_full(w, 31)
+
+
+@pytest.mark.parametrize("w", FOUR_WAVE, ids=_ids(FOUR_WAVE))
+def test_four_wave_single_pass_shapes(w):
+    import online_softmax_10_amd as osa
+
+    assert osa.plan(w.B, w.H, w.N, w.M, w.d, w.dtype) == ("attn_fwd_bf16_kernel", 1)
+    check_full(w, 32)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_halves_scores_far_below_zero(d, causal):
+    # test_scores_far_below_zero on the key-halves kernel: each set of waves
+    # sets its rows' shifts from its own first tile
+    import online_softmax_10_amd as osa
+
+    w = si.Workload("negscores", 1, 2, 300, 1100, d, "bf16", causal, "normal")
+    assert osa.plan(w.B, w.H, w.N, w.M, w.d, w.dtype)[0] == "attn_fwd_bf16_kh_kernel"
+    rng = np.random.default_rng(13)
+    a = np.sqrt(300.0 / (d * float(w.scale)))
+    q = (a + 0.3 * rng.standard_normal((w.B, w.H, w.N, d))).astype(np.float32)
+    k = (-a + 0.3 * rng.standard_normal((w.B, w.H, w.M, d))).astype(np.float32)
+    v = rng.standard_normal((w.B, w.H, w.M, d)).astype(np.float32)
+    check_full(w, 13, qkv=tuple(si.f32_to_bf16_bits(x) for x in (q, k, v)))
+
+
+def test_key_halves_peaked_large_values():
+    # test_peaked_softmax_large_values on the key-halves kernel: the two sets
+    # of waves reach different shifts, which the merge reconciles
+    import online_softmax_10_amd as osa
+
+    w = W["c4"].with_shape(H=4, N=512, M=2048)
+    assert osa.plan(w.B, w.H, w.N, w.M, w.d, w.dtype)[0] == "attn_fwd_bf16_kh_kernel"
+    q, k, v = si.make_qkv(w, 8)
+    v_big = si.f32_to_bf16_bits(si.to_f64(v, "bf16").astype(np.float32) * np.float32(2.0 ** 50))
+    log("[gpu] peaked softmax, V scaled by 2^50, key halves")
+    o, lse = gpu_attention(q, k, v_big, "bf16", w.scale, True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    o_ref, lse_ref = oracle.attention(si.to_f64(q, "bf16"), si.to_f64(k, "bf16"), si.to_f64(v, "bf16"), w.scale, True)
+    compare(o / 2.0 ** 50, lse, o_ref, lse_ref, "bf16", "peaked, V x 2^50, key halves")

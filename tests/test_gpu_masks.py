@@ -59,6 +59,10 @@ CASES = [
     (W("m", 4, 4, 1, 5000, 128, "bf16", True, "normal"), "bottom_right", [4000, 123, 5000, 0], 0),
     (W("m", 2, 4, 4, 3000, 64, "bf16", True, "normal"), "bottom_right", [3000, 1], 0),
     (W("m", 2, 2, 3, 900, 128, "f32", False, "normal"), False, [899, 2], 0),
+    # key halves (few 128-row workgroups, long key ranges): a key length that
+    # leaves the second set of waves one tile fewer, a single key, none
+    (W("m", 2, 2, 300, 1000, 64, "bf16", True, "normal"), "bottom_right", [1000, 413], 0),
+    (W("m", 3, 2, 200, 1100, 128, "bf16", True, "normal"), "top_left", [0, 1, 1100], 0),
     # 256-row widths (>= 256 workgroups of 256 rows): eight waves at d = 64,
     # 64 rows per wave at d = 128
     (W("m", 2, 128, 512, 700, 64, "bf16", True, "normal"), "bottom_right", [700, 301], 0),

@@ -3,8 +3,8 @@ accumulation's precision, so the workloads' bf16 bound holds literally --
 max |o - o_ref| <= 1e-2 and max |lse - lse_ref| <= 5e-3, without the half
 bf16 ulp that storing O in bf16 adds -- including the long-context workload
 (|O| up to ~5.7, where rounding to bf16 alone moves O by up to 0.0156).  And
-on every path (eight- and four-wave single pass, split partials, decode,
-bias) rounding the float32 output to bf16 gives exactly the bf16 output."""
+on every path (eight-wave, key-halves and four-wave single pass, split
+partials, decode, bias) rounding the float32 output to bf16 gives exactly the bf16 output."""
 
 import numpy as np
 import pytest
@@ -57,7 +57,9 @@ def test_literal_bf16_bound_with_f32_output(wl, count):
 CASES = [
     # (workload, splits, extra)
     (si.Workload("f", 2, 16, 2048, 2048, 128, "bf16", True, "normal"), 0, {}),          # eight-wave
-    (si.Workload("f", 2, 4, 700, 900, 64, "bf16", False, "normal"), 1, {}),             # four-wave single
+    (si.Workload("f", 2, 4, 700, 900, 64, "bf16", False, "normal"), 1, {}),             # key halves
+    (si.Workload("f", 1, 4, 300, 1000, 128, "bf16", True, "normal"), 0, {}),            # key halves, causal
+    (si.Workload("f", 1, 100, 384, 300, 64, "bf16", True, "normal"), 0, {}),            # four-wave single
     (si.Workload("f", 1, 2, 130, 3000, 128, "bf16", True, "normal"), 5, {}),            # split partials
     (si.Workload("f", 4, 8, 3, 5000, 128, "bf16", False, "normal"), 0, {}),             # decode
     (si.Workload("f", 2, 128, 300, 520, 128, "bf16", True, "normal"), 0, {"bias": 1}),  # bias, large
