@@ -386,28 +386,82 @@ struct WaveTile {
     // region.
     __device__ __forceinline__ void store_rows(int N, int q_wave, uint16_t *o_head, float *lse_head, char *region,
                                                int lane) {
-        constexpr int CPR = D / 8;      // 16-byte chunks per row
+        store_cols<0, D / 32>(N, q_wave, o_head, lse_head, region, lane, true);
+    }
+
+    // store_rows for the 32-column blocks [B0, B0 + NB) of the rows only (the
+    // staged tile is 32 x 32*NB); the LSE is written if write_lse.
+    template <int B0, int NB>
+    __device__ __forceinline__ void store_cols(int N, int q_wave, uint16_t *o_head, float *lse_head, char *region,
+                                               int lane, bool write_lse) {
+        constexpr int W = 32 * NB;      // columns stored
+        constexpr int CPR = W / 8;      // 16-byte chunks per staged row
         constexpr int ROWS = 64 / CPR;  // rows per store instruction
         const float l_tot = xhalf_sum(l_run);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (qrow < N && hh == 0) lse_head[qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2 : NEG_INF;
+        if (write_lse && qrow < N && hh == 0) lse_head[qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2 : NEG_INF;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                f32x4 x = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv, oacc[db][4 * g + 2] * inv,
-                           oacc[db][4 * g + 3] * inv};
-                const int chunk = (4 * db + g) ^ (l32 % CPR);
-                *reinterpret_cast<bf16x4 *>(region + l32 * (2 * D) + chunk * 16 + 8 * hh) = __builtin_convertvector(x, bf16x4);
+                const f32x16 &a = oacc[B0 + b];
+                f32x4 x = {a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
+                const int chunk = (4 * b + g) ^ (l32 % CPR);
+                *reinterpret_cast<bf16x4 *>(region + l32 * (2 * W) + chunk * 16 + 8 * hh) = __builtin_convertvector(x, bf16x4);
             }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
         const int c = lane % CPR;
 #pragma unroll
         for (int i = 0; i < 32 / ROWS; ++i) {
             const int r = lane / CPR + ROWS * i;
-            const u32x4 val = *reinterpret_cast<const u32x4 *>(region + r * (2 * D) + ((c ^ (r % CPR)) * 16));
-            if (q_wave + r < N) *reinterpret_cast<u32x4 *>(o_head + (size_t)(q_wave + r) * D + 8 * c) = val;
+            const u32x4 val = *reinterpret_cast<const u32x4 *>(region + r * (2 * W) + ((c ^ (r % CPR)) * 16));
+            if (q_wave + r < N) *reinterpret_cast<u32x4 *>(o_head + (size_t)(q_wave + r) * D + 32 * B0 + 8 * c) = val;
         }
+    }
+
+    // Key halves: this wave's accumulator blocks [B0, B0 + NB) for its
+    // partner wave (the other set, same rows) into xfer, 16 bytes per lane per
+    // instruction (conflict-free).
+    template <int B0, int NB>
+    __device__ __forceinline__ void put_blocks(char *xfer, int lane) const {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16 &a = oacc[B0 + b];
+                *reinterpret_cast<f32x4 *>(xfer + (4 * b + g) * 1024 + 16 * lane) =
+                    f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+            }
+    }
+
+    // ... and the merge of the partner's state into this wave's: blocks
+    // [B0, B0 + NB) from xfer (as put_blocks wrote them), the partner's shift
+    // m_o and sum share l_o; the rule for two blocks of keys (the larger
+    // shift, each side scaled by 2^(its shift - that one); a side without a
+    // key (shift -inf) weighs 0).  Both waves of a pair evaluate every sum in
+    // the same order, set 0's term first (SET0: this wave is in set 0), so
+    // that whichever stores a column gives the same bits.
+    template <int B0, int NB, bool SET0>
+    __device__ __forceinline__ void merge_blocks(const char *xfer, float m_o, float l_o, int lane) {
+        const float mm = fmaxf(m_run, m_o);
+        const float w_me = m_run == NEG_INF ? 0.f : exp2_fast(m_run - mm);
+        const float w_o = m_o == NEG_INF ? 0.f : exp2_fast(m_o - mm);
+        const float w0 = SET0 ? w_me : w_o, w1 = SET0 ? w_o : w_me;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(xfer + (4 * b + g) * 1024 + 16 * lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float mine = oacc[B0 + b][4 * g + i];
+                    const float x0 = SET0 ? mine : y[i], x1 = SET0 ? y[i] : mine;
+                    oacc[B0 + b][4 * g + i] = __builtin_fmaf(x0, w0, x1 * w1);
+                }
+            }
+        const float l0 = SET0 ? l_run : l_o, l1 = SET0 ? l_o : l_run;
+        l_run = __builtin_fmaf(l0, w0, l1 * w1);
+        m_run = mm;
     }
 
     // Final o = o~ / l and LSE; bf16 output or fp32 split partial.
