@@ -84,12 +84,14 @@ def test_two_streams_at_once():
             assert torch.equal(outs[i][0], refs[i][0]) and torch.equal(outs[i][1], refs[i][1]), (rep, i)
 
 
-def test_graph_capture_and_replay():
+@pytest.mark.parametrize("shape", [(2, 8, 512, 768, 128), (1, 4, 512, 1024, 64)], ids=["four_wave", "key_halves"])
+def test_graph_capture_and_replay(shape):
     import torch
 
     import online_softmax_10_amd as osa
 
-    w = si.Workload("g", 2, 8, 512, 768, 128, "bf16", True, "normal")
+    B, H, N, M, d = shape
+    w = si.Workload("g", B, H, N, M, d, "bf16", True, "normal")
     q, k, v = _inputs(w, 20)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
