@@ -7,28 +7,37 @@
 // ("Softmax与Flash-Attention" page, FlashAttention core idea), with the
 // query-outer loop order of its v2 section.
 //
-// One kernel body, two widths:
-//   attn_fwd_bf16_kernel     4 waves, 128 query rows per workgroup, two
-//                            workgroups per CU (small problems, split partials);
+// One kernel body, three forms:
 //   attn_fwd_bf16_w8_kernel  8 waves, 256 query rows per workgroup, one per CU
 //                            (problems whose 256-row tiles fill the chip; single
 //                            pass), so a K/V tile crosses L2 -> LDS once per 256
-//                            rows.
-// Either way each SIMD runs two waves.  attn_fwd_bf16_bias_kernel is the
-// four-wave width with an additive score bias (one workgroup per CU at
-// d = 128, where its bias prefetch does not fit at two).
+//                            rows;
+//   attn_fwd_bf16_kh_kernel  8 waves on 128 query rows, in two sets of four that
+//                            take alternate key tiles (each with its own K/V
+//                            stages) and merge their states at the end (problems
+//                            whose 128-row tiles number at most 256: one per CU;
+//                            single pass);
+//   attn_fwd_bf16_kernel     4 waves, 128 query rows per workgroup, two
+//                            workgroups per CU (the other problems, split
+//                            partials).
+// Each SIMD runs two waves.  attn_fwd_bf16_w8_bias_kernel and
+// attn_fwd_bf16_bias_kernel are the 256- and 128-row forms with an additive
+// score bias.
 //
 // Software pipeline.  Iteration j of a wave's key loop, with the scores
-// S(j) of tile j already in registers:
+// S(j) of tile j already in registers, shifted and masked:
 //   - one wait + barrier: K(j+1) and V(j) have landed in LDS, and every wave
 //     is done with the stages the iteration's loads overwrite;
 //   - the 16 score MFMAs of S(j+1) = K(j+1) Q^T, each followed by the K
-//     operand read two MFMAs ahead and by the softmax work of two scores of
-//     tile j (FMA, exp2, bf16 pack, dot2 into the sum), so the matrix cores
-//     and the VALU work side by side; K(j+2) and V(j+1) are loaded between;
+//     operand read two MFMAs ahead and by the probabilities of tile j's
+//     remaining scores (exp2, bf16 pack, dot2 into the sum), so the matrix
+//     cores and the VALU work side by side; K(j+2) and V(j+1) are loaded
+//     between;
 //   - the rare exact-shift path (attn_bf16_common.h);
 //   - the 16 MFMAs of O^T += V(j)^T P(j)^T with the transposed V reads two
-//     MFMAs ahead.
+//     MFMAs ahead, each followed by the shift (and on diagonal tiles the
+//     mask) of two of tile j+1's scores and, in the first slots, the
+//     probabilities of its first pairs.
 // sched_barrier fences keep this order: the compiler's own schedule puts the
 // MFMAs and the softmax in separate runs.  K/V tiles of 64 keys go HBM -> LDS
 // by LDS-direct buffer loads into two stages each; the buffer range check
