@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
     "attn_fwd_bf16_w8_kernel": BF16_SOURCES,
     "attn_fwd_bf16_kernel": BF16_SOURCES,
     "attn_fwd_bf16_kh_kernel": BF16_SOURCES,
+    "attn_fwd_bf16_kh_bias_kernel": BF16_SOURCES,
     "attn_decode_kernel": ["attn_decode.hip"],
     "attn_fwd_f32_small_kernel": ["attn_f32.hip"],
     "attn_fwd_f32_kernel": ["attn_f32.hip"],
@@ -619,7 +620,9 @@ def main() -> int:
         if w.dtype != "bf16":
             kernel = "attn_fwd_f32_kernel"
         else:
-            kernel = "attn_fwd_bf16_w8_bias_kernel" if kernel == "attn_fwd_bf16_w8_kernel" else "attn_fwd_bf16_bias_kernel"
+            kernel = {"attn_fwd_bf16_w8_kernel": "attn_fwd_bf16_w8_bias_kernel",
+                      "attn_fwd_bf16_kh_kernel": "attn_fwd_bf16_kh_bias_kernel" if w.d == 64
+                      else "attn_fwd_bf16_bias_kernel"}.get(kernel, "attn_fwd_bf16_bias_kernel")
         abytes += w.N * w.M * 4  # the broadcast bias, read once
     achieved = w.flops / (launch_ms * 1e-3) / 1e12
     gbs = abytes / (launch_ms * 1e-3) / 1e9

@@ -38,7 +38,8 @@ int osa::launch_planned(const osa::PlannedCall &plan, void *workspace, hipStream
         const hipError_t e = plan.kernel == osa::MainKernel::F32         ? osa::launch_attn_f32(p, stream)
                              : plan.kernel == osa::MainKernel::F32_SMALL ? osa::launch_attn_f32_small(p, stream)
                              : w8                                        ? osa::launch_attn_bf16_w8(p, stream)
-                             : plan.kernel == osa::MainKernel::BF16_KH   ? osa::launch_attn_bf16_kh(p, stream)
+                             : plan.kernel == osa::MainKernel::BF16_KH || plan.kernel == osa::MainKernel::BF16_KH_BIAS
+                                 ? osa::launch_attn_bf16_kh(p, stream)
                                                                          : osa::launch_attn_bf16(p, stream);
         if (e != hipSuccess) {
             set_detail("attention kernel launch", e);

@@ -102,7 +102,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     // KH = 2: the workgroup holds two sets of NW waves on the same rows, set
     // h taking the key tiles t = 2j + h of the range, each with its own LDS
     // stages; their states are merged at the end.
-    static_assert(KH == 1 || (KH == 2 && !BIAS), "key halves: no bias");
+    static_assert(KH == 1 || (KH == 2 && (!BIAS || D == 64)), "key halves: a bias only at d = 64 (LDS)");
     __shared__ __attribute__((aligned(1024))) char lds_k0[KH * T::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_k1[KH * T::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_v0[KH * T::BYTES];
@@ -151,8 +151,8 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
     uint32_t brow = 0;
     char *bregion = nullptr;  // this wave's 8 KiB bias stage in LDS
     if constexpr (BIAS) {
-        __shared__ __attribute__((aligned(1024))) char lds_b[NW * 8192];
-        bregion = lds_b + wave * 8192;
+        __shared__ __attribute__((aligned(1024))) char lds_b[KH * NW * 8192];
+        bregion = lds_b + wave_all * 8192;
         brs = make_rsrc(bias, bias_bytes);
         brow = 4u * (uint32_t)((int64_t)(bh / H) * bias_sb + (int64_t)(bh % H) * bias_sh +
                                (int64_t)min(wt.qrow, N - 1) * bias_sn);
@@ -319,7 +319,7 @@ __device__ __forceinline__ void attn_body(const uint16_t *__restrict__ q, const 
         for (int i = 0; i < LOADS; ++i)
             if (ntiles > 0) load(krs, 0, k0, i);
         if constexpr (BIAS) {
-            if (nw > 0) wt.bias_dma(brs, brow, kb, bregion);
+            if (nw > 0) wt.bias_dma(brs, brow, tkey(0), bregion);
         }
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
@@ -500,6 +500,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_w8_bias_kernel(ATTN_BIAS
     attn_body<8, D, CAUSAL, SPLIT, true>(ATTN_KERNEL_PASS, bias, bias_bytes, bias_sb, bias_sh, bias_sn);
 }
 
+// Key halves with a bias, at d = 64 (each of the eight waves has its own bias
+// stage: 64 KiB of LDS beside the 64 KiB of K/V stages).
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kh_bias_kernel(ATTN_BIAS_ARGS) {
+    attn_body<4, 64, CAUSAL, false, true, 2>(ATTN_KERNEL_PASS, bias, bias_bytes, bias_sb, bias_sh, bias_sn);
+}
+
 template <int NW, int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_t(const AttnProblem &p, hipStream_t stream) {
     const int rows = 32 * NW;
@@ -552,6 +559,17 @@ hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream) {
 template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_kh_t(const AttnProblem &p, hipStream_t stream) {
     const int ntq = (p.N + 127) / 128;
+    if constexpr (D == 64 && !SPLIT) {
+        if (p.bias != nullptr) {
+            hipLaunchKernelGGL((attn_fwd_bf16_kh_bias_kernel<CAUSAL>), dim3((unsigned)((int64_t)p.BH * ntq)), dim3(512),
+                               0, stream, static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                               static_cast<const uint16_t *>(p.v), static_cast<uint16_t *>(p.o), p.lse, p.part_o,
+                               p.part_lse, p.BH, p.N, p.M, p.c, p.negate_q ? 0x80008000u : 0u, ntq, 1,
+                               p.tiles_per_split, p.kv_len, p.H, p.causal_off, p.bias, p.bias_bytes, p.bias_sb,
+                               p.bias_sh, p.bias_sn);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((attn_fwd_bf16_kh_kernel<D, CAUSAL, SPLIT>), dim3((unsigned)((int64_t)p.BH * ntq)), dim3(512), 0,
                        stream, static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                        static_cast<const uint16_t *>(p.v), static_cast<uint16_t *>(p.o), p.lse, p.part_o, p.part_lse,
@@ -573,8 +591,9 @@ hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_attn_bf16_kh(const AttnProblem &p, hipStream_t stream) {
-    // Single pass (a float32 o through the partial-store form), no bias.
-    if (p.splits != 1 || p.bias != nullptr) return hipErrorInvalidValue;
+    // Single pass (a float32 o through the partial-store form); a bias only
+    // at d = 64 with a bf16 o.
+    if (p.splits != 1 || (p.bias != nullptr && (p.d != 64 || p.out_f32))) return hipErrorInvalidValue;
     if (p.out_f32) {
         if (p.d == 64) return p.causal ? launch_kh_t<64, true, true>(p, stream) : launch_kh_t<64, false, true>(p, stream);
         return p.causal ? launch_kh_t<128, true, true>(p, stream) : launch_kh_t<128, false, true>(p, stream);

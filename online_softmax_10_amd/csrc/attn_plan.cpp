@@ -125,9 +125,12 @@ MainKernel main_kernel(const Plan &plan, int64_t BH, int64_t N, int64_t M, int d
     // four-wave width on 4x8x1024xM, d = 64: M = 384 +5.5 %, 512 +2 %, 640
     // +1 %, 768 -1.5 %, 1024 -4 % (causal -8 %); d = 128: M = 512 +6 %, 1024
     // -0.3 % (1x16x1024^2: -3 %, causal -4 %).
-    if (plan.kind == Plan::SINGLE && !bias && BH * ceil_div(N, 128) <= 256 &&
+    // With a bias only at d = 64, where the eight waves' bias stages fit in
+    // LDS beside the K/V stages (and never with a float32 o and a bias, taken
+    // above).
+    if (plan.kind == Plan::SINGLE && (!bias || d == 64) && BH * ceil_div(N, 128) <= 256 &&
         ceil_div(M, kBf16KeyTile) >= (d == 64 ? kBf16KhMinTiles64 : kBf16KhMinTiles128))
-        return MainKernel::BF16_KH;
+        return bias ? MainKernel::BF16_KH_BIAS : MainKernel::BF16_KH;
     return bias ? MainKernel::BF16_BIAS : MainKernel::BF16_4W;
 }
 
@@ -143,6 +146,7 @@ const char *main_kernel_name(MainKernel k) {
     case MainKernel::DECODE: return "attn_decode_kernel";
     case MainKernel::BF16_BIAS: return "attn_fwd_bf16_bias_kernel";
     case MainKernel::BF16_8W_BIAS: return "attn_fwd_bf16_w8_bias_kernel";
+    case MainKernel::BF16_KH_BIAS: return "attn_fwd_bf16_kh_bias_kernel";
     }
     return "";
 }

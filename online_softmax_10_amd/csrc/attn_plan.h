@@ -54,7 +54,7 @@ constexpr int kF32SmallMaxKeys = 1024;  // keys the small fp32 kernel takes (its
 
 // The kernel that carries the attention itself (the split paths add the
 // merge kernel).
-enum class MainKernel { F32, F32_SMALL, BF16_4W, BF16_8W, BF16_KH, DECODE, BF16_BIAS, BF16_8W_BIAS };
+enum class MainKernel { F32, F32_SMALL, BF16_4W, BF16_8W, BF16_KH, DECODE, BF16_BIAS, BF16_8W_BIAS, BF16_KH_BIAS };
 const char *main_kernel_name(MainKernel k);
 
 struct PlannedCall {

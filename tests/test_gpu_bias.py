@@ -61,6 +61,11 @@ CASES = [
     (W("b", 1, 1, 256, 256, 64, "f32", False, "uniform01"), False, (1, 1, 256, 256), "normal", None, 0, 0.0),
     (W("b", 2, 2, 100, 301, 128, "f32", True, "normal"), "bottom_right", (2, 2, 100, 301), "normal", None, 2, 0.2),
     (W("b", 1, 8, 1024, 1024, 128, "bf16", True, "normal"), True, (1, 8, 1024, 1024), "distance", None, 0, 0.0),
+    # key halves with a bias (d = 64, few 128-row tiles, long key ranges)
+    (W("b", 2, 2, 300, 1000, 64, "bf16", True, "normal"), "bottom_right", (2, 2, 300, 1000), "normal", [1000, 555], 0,
+     0.1),
+    (W("b", 1, 4, 200, 900, 64, "bf16", False, "normal"), False, (1, 4, 200, 900), "distance", None, 0, 0.0),
+    (W("b", 1, 2, 129, 1025, 64, "bf16", True, "normal"), True, (1, 2, 1, 1025), "normal", None, 0, 0.0),
 ]
 
 
@@ -71,11 +76,12 @@ def test_bias_matches_oracle(w, causal, bshape, kind, kv_len, splits, frac):
     run_bias(w, causal, bshape, kind, kv_len, splits, frac)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
-def test_bias_dead_row(dtype, d):
-    # One row's bias is -inf at every key: o = 0, lse = -inf for it alone.
-    w = W("b", 2, 2, 70, 150, d, dtype, False, "normal")
-    assert run_bias(w, False, (2, 2, 70, 150), dead=(1, 0, 33)) == 1
+@pytest.mark.parametrize("dtype,d,M", [("bf16", 128, 150), ("bf16", 64, 150), ("f32", 64, 150), ("bf16", 64, 1000)])
+def test_bias_dead_row(dtype, d, M):
+    # One row's bias is -inf at every key: o = 0, lse = -inf for it alone
+    # (M = 1000 at d = 64: the key-halves kernel, both sets without a key).
+    w = W("b", 2, 2, 70, M, d, dtype, False, "normal")
+    assert run_bias(w, False, (2, 2, 70, M), dead=(1, 0, 33)) == 1
 
 
 def test_zero_bias_equals_no_bias():
