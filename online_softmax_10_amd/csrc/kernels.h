@@ -22,8 +22,8 @@ hipError_t launch_attn_bf16(const AttnProblem &p, hipStream_t stream);
 hipError_t launch_attn_bf16_w8(const AttnProblem &p, hipStream_t stream);
 // Key-halves bf16 kernel: 128 query rows per workgroup of eight waves, the
 // key tiles alternating between two sets of four waves and merged in LDS;
-// single pass (bf16 output, or a float32 one through the partial-store form),
-// no bias.
+// single pass (bf16 output, or a float32 one through the partial-store form);
+// an additive bias at d = 64 with a bf16 output.
 hipError_t launch_attn_bf16_kh(const AttnProblem &p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnProblem &p, hipStream_t stream);
 // fp32, small problems: one workgroup per 16-row block, keys split over its
